@@ -1,0 +1,277 @@
+"""Seeded synthetic inputs for the DSA step, shared by the tests, the smoke
+check and the benchmark.
+
+This module only draws random numbers and packs them into the byte layouts
+the library and the oracle both read. It holds none of the step's arithmetic
+(no scores, no selection, no attention). The one transformation it applies is
+the input convention of the indexer: the SGLang indexer page quantizes the
+index query per 128-wide row with `act_quant(..., block_size=128)` and folds
+the resulting scale into the head weights (`_get_logits_head_gate`), and
+stores each index key as fp8 plus one fp32 scale (`_store_index_k_cache`).
+Those quantizations happen before the step and are done here on the CPU with
+torch's float8_e4m3fn conversion so that both sides consume identical bytes.
+
+Draw order (numpy `default_rng(seed)`), fixed so the bytes are reproducible:
+1. context lengths (only for configs with a length range);
+2. page permutation of the pool; unused block-table slots point at one
+   extra poison page filled with NaN;
+3. index keys, standard normal [pages, P, D];
+4. index queries, standard normal [T, H, D];
+5. head weights, standard normal [T, H] / sqrt(H);
+6. latent cache, standard normal [pages, P, Dl + Dr];
+7. MLA queries, standard normal [T, Hm, Dl + Dr].
+Slots past a request's length inside its last page are NaN canaries.
+"""
+
+from dataclasses import dataclass, field
+import math
+
+import numpy as np
+
+F8_MAX = 448.0
+NAN_F8 = 0x7F
+NAN_BF16 = 0x7FC0
+
+
+@dataclass(frozen=True)
+class Config:
+    name: str
+    seed: int
+    batch: int
+    ctx: tuple = ()                 # fixed key lengths per request (decode) or ()
+    ctx_range: tuple = ()           # (lo, hi) inclusive uniform lengths when ctx == ()
+    q_lens: tuple = ()              # rows per request; () = decode (one row each)
+    page_size: int = 64
+    idx_heads: int = 64
+    idx_dim: int = 128
+    idx_kind: str = "fp8"           # "fp8" (quantized) or "f32"
+    topk: int = 2048
+    mla_heads: int = 128
+    d_latent: int = 512
+    d_rope: int = 64
+    mla_kind: str = "bf16"          # "bf16" or "f32"
+    softmax_scale: float = 1.0 / math.sqrt(192.0)
+    note: str = ""
+
+    @property
+    def is_prefill(self):
+        return len(self.q_lens) > 0
+
+
+# The five workloads the step is specified on, plus the literal "ctx 32k"
+# variant of the ragged decode batch.
+CONFIGS = {
+    "tiny": Config("tiny", seed=0, batch=1, ctx=(256,), page_size=16, idx_heads=4,
+                   idx_dim=32, idx_kind="f32", topk=64, mla_heads=8, d_latent=64,
+                   d_rope=16, mla_kind="f32", softmax_scale=1.0 / math.sqrt(80.0),
+                   note="batch 1 decode, ctx 256, fp32, 4x32 indexer, 8-head 80-d MLA"),
+    "decode_b1_8k": Config("decode_b1_8k", seed=1, batch=1, ctx=(8192,),
+                           note="DeepSeek-V3.2-shaped single decode, ctx 8192"),
+    "decode_b64_ragged": Config("decode_b64_ragged", seed=2, batch=64, ctx_range=(4096, 32768),
+                                note="ragged batch-64 decode, ctx U[4096, 32768]"),
+    "decode_b8_128k": Config("decode_b8_128k", seed=3, batch=8, ctx=(131072,) * 8,
+                             note="batch-8 decode, ctx 131072"),
+    "prefill_4k_on_16k": Config("prefill_4k_on_16k", seed=4, batch=1, ctx=(20480,), q_lens=(4096,),
+                                note="chunked prefill: 4096 rows on a 16384 prefix"),
+    "decode_b64_32k": Config("decode_b64_32k", seed=5, batch=64, ctx=(32768,) * 64,
+                             note="batch-64 decode, every ctx 32768"),
+}
+
+
+@dataclass
+class Workload:
+    cfg: Config
+    seq_lens_k: np.ndarray          # int32 [B]
+    cu_seqlens_q: object            # int32 [B+1] or None (decode)
+    block_table: np.ndarray         # int32 [B, max_pages]
+    num_pages: int                  # pages in the pool, poison page included
+    index_cache: np.ndarray         # uint8 [num_pages, page_bytes]
+    q_idx: np.ndarray               # uint8 fp8 codes or float32 [T, H, D]
+    w: np.ndarray                   # float32 [T, H] (q scale folded in)
+    latent: np.ndarray              # uint16 bf16 bits or float32 [num_pages, P, Dqk]
+    q_mla: np.ndarray               # uint16 bf16 bits or float32 [T, Hm, Dqk]
+    extras: dict = field(default_factory=dict)
+
+    @property
+    def num_rows(self):
+        return self.q_idx.shape[0]
+
+    @property
+    def max_seq_len_k(self):
+        return int(self.seq_lens_k.max()) if len(self.seq_lens_k) else 0
+
+    @property
+    def max_seq_len_q(self):
+        if self.cu_seqlens_q is None:
+            return 1
+        return int(np.diff(self.cu_seqlens_q).max()) if len(self.seq_lens_k) else 0
+
+
+def _to_bf16_bits(x32):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _bf16_bits_to_f32(bits):
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _to_e4m3fn_bytes(x32):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _normal_chunks(rng, shape, chunk_rows):
+    """standard_normal(shape) drawn in slices of the leading dim; the
+    generator's stream is the same as one call of the whole shape."""
+    out = np.empty(shape, dtype=np.float32)
+    for s in range(0, shape[0], chunk_rows):
+        e = min(shape[0], s + chunk_rows)
+        out[s:e] = rng.standard_normal((e - s,) + tuple(shape[1:]))
+    return out
+
+
+def generate(cfg, with_mla=True, with_indexer=True):
+    """Build the seeded inputs of `cfg` (a Config or a CONFIGS key)."""
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    rng = np.random.default_rng(cfg.seed)
+    B, P = cfg.batch, cfg.page_size
+
+    # 1. context lengths
+    if cfg.ctx:
+        lens = np.asarray(cfg.ctx, dtype=np.int64)
+    else:
+        lo, hi = cfg.ctx_range
+        lens = rng.integers(lo, hi, size=B, endpoint=True)
+    assert len(lens) == B
+    if cfg.is_prefill:
+        q_lens = np.asarray(cfg.q_lens, dtype=np.int64)
+        cu = np.zeros(B + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(q_lens)
+        T = int(cu[-1])
+    else:
+        cu = None
+        T = B
+
+    # 2. pages
+    n_pages = [max(1, -(-int(n) // P)) for n in lens]
+    total = int(sum(n_pages))
+    poison = total
+    pool = rng.permutation(total)
+    max_pages = max(n_pages)
+    block_table = np.full((B, max_pages), poison, dtype=np.int32)
+    off = 0
+    for b, n in enumerate(n_pages):
+        block_table[b, :n] = pool[off:off + n]
+        off += n
+    num_pages = total + 1
+    # which (page, slot) pairs hold real tokens
+    live = np.zeros((num_pages, P), dtype=bool)
+    for b in range(B):
+        for p in range(n_pages[b]):
+            page = block_table[b, p]
+            cnt = min(P, int(lens[b]) - p * P)
+            if cnt > 0:
+                live[page, :cnt] = True
+
+    H, D = cfg.idx_heads, cfg.idx_dim
+    # 3. index keys (+ per-token scale)
+    if with_indexer:
+        keys = _normal_chunks(rng, (total, P, D), 256)
+        if cfg.idx_kind == "fp8":
+            amax = np.abs(keys).max(axis=2)
+            sigma = (np.maximum(amax, np.float32(1e-30)) / np.float32(F8_MAX)).astype(np.float32)
+            codes = np.full((num_pages, P, D), NAN_F8, dtype=np.uint8)
+            for s in range(0, total, 4096):
+                e = min(total, s + 4096)
+                codes[s:e] = _to_e4m3fn_bytes(keys[s:e] / sigma[s:e, :, None])
+            sig_all = np.full((num_pages, P), np.nan, dtype=np.float32)
+            sig_all[:total] = sigma
+            # canaries: NaN keys and scales in dead slots and in the poison page
+            codes[~live] = NAN_F8
+            sig_all[~live] = np.nan
+            page_bytes = P * D + 4 * P
+            cache = np.empty((num_pages, page_bytes), dtype=np.uint8)
+            cache[:, :P * D] = codes.reshape(num_pages, P * D)
+            cache[:, P * D:] = sig_all.view(np.uint8).reshape(num_pages, 4 * P)
+            del codes
+        else:
+            page_bytes = 4 * P * D + 4 * P
+            cache = np.empty((num_pages, page_bytes), dtype=np.uint8)
+            kf = np.full((num_pages, P, D), np.nan, dtype=np.float32)
+            kf[:total] = keys
+            kf[~live] = np.nan
+            sf = np.ones((num_pages, P), dtype=np.float32)
+            sf[~live] = np.nan
+            cache[:, :4 * P * D] = kf.reshape(num_pages, -1).view(np.uint8)
+            cache[:, 4 * P * D:] = sf.view(np.uint8)
+        del keys
+
+        # 4. index queries, 5. head weights
+        qn = _normal_chunks(rng, (T, H, D), 1024)
+        wn = (rng.standard_normal((T, H)) / math.sqrt(H)).astype(np.float32)
+        if cfg.idx_kind == "fp8":
+            qb = _bf16_bits_to_f32(_to_bf16_bits(qn))           # q is bf16 before quantization
+            amax = np.abs(qb).max(axis=2)
+            s_q = (np.maximum(amax, np.float32(1e-30)) / np.float32(F8_MAX)).astype(np.float32)
+            q_idx = np.empty((T, H, D), dtype=np.uint8)
+            for s in range(0, T, 1024):
+                e = min(T, s + 1024)
+                q_idx[s:e] = _to_e4m3fn_bytes(qb[s:e] / s_q[s:e, :, None])
+            w = (wn * s_q).astype(np.float32)                   # fold the q scale into the gate
+        else:
+            q_idx = qn.astype(np.float32)
+            w = wn
+        del qn
+    else:
+        cache = np.zeros((num_pages, 0), dtype=np.uint8)
+        q_idx = np.zeros((T, H, D), dtype=np.uint8 if cfg.idx_kind == "fp8" else np.float32)
+        w = np.zeros((T, H), dtype=np.float32)
+
+    # 6. latent cache, 7. MLA queries
+    Dqk = cfg.d_latent + cfg.d_rope
+    Hm = cfg.mla_heads
+    if with_mla:
+        if cfg.mla_kind == "bf16":
+            latent = np.empty((num_pages, P, Dqk), dtype=np.uint16)
+            for s in range(0, total, 512):
+                e = min(total, s + 512)
+                latent[s:e] = _to_bf16_bits(rng.standard_normal((e - s, P, Dqk)).astype(np.float32))
+            latent[total:] = NAN_BF16
+            latent[~live] = NAN_BF16
+            q_mla = np.empty((T, Hm, Dqk), dtype=np.uint16)
+            for s in range(0, T, 256):
+                e = min(T, s + 256)
+                q_mla[s:e] = _to_bf16_bits(rng.standard_normal((e - s, Hm, Dqk)).astype(np.float32))
+        else:
+            latent = np.full((num_pages, P, Dqk), np.nan, dtype=np.float32)
+            latent[:total] = rng.standard_normal((total, P, Dqk)).astype(np.float32)
+            latent[~live] = np.nan
+            q_mla = rng.standard_normal((T, Hm, Dqk)).astype(np.float32)
+    else:
+        latent = np.zeros((num_pages, P, 0), dtype=np.uint16)
+        q_mla = np.zeros((T, Hm, 0), dtype=np.uint16)
+
+    return Workload(cfg=cfg, seq_lens_k=lens.astype(np.int32), cu_seqlens_q=cu,
+                    block_table=block_table, num_pages=num_pages, index_cache=cache,
+                    q_idx=q_idx, w=w, latent=latent, q_mla=q_mla)
+
+
+def small_config(name, seed, lens, q_lens=(), page_size=64, topk=2048, idx_kind="fp8",
+                 mla_kind="bf16", **kw):
+    """A reduced workload with the DeepSeek shapes (or fp32 shapes) and the
+    given lengths, for parity tests the oracle finishes in seconds."""
+    if idx_kind == "f32":
+        kw.setdefault("idx_heads", 4)
+        kw.setdefault("idx_dim", 32)
+    if mla_kind == "f32":
+        kw.setdefault("mla_heads", 8)
+        kw.setdefault("d_latent", 64)
+        kw.setdefault("d_rope", 16)
+        kw.setdefault("softmax_scale", 1.0 / math.sqrt(80.0))
+    return Config(name, seed=seed, batch=len(lens), ctx=tuple(int(x) for x in lens),
+                  q_lens=tuple(int(x) for x in q_lens), page_size=page_size, topk=topk,
+                  idx_kind=idx_kind, mla_kind=mla_kind, **kw)
