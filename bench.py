@@ -1,0 +1,216 @@
+"""Benchmark of one DSA decode step (indexer -> top-k -> sparse MLA) on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one batch: dsa_indexer_logits,
+dsa_topk and sparse_mla_decode (with its split-KV combine) on one stream. The
+inputs are generated on the host, copied to HBM before timing, and stay
+resident. Prints one JSON line:
+
+* value: decode tokens/s = rows per step / step time (one token per request);
+* sparse_attn_hbm_gbps: algorithmic sparse-attention bytes / attention time;
+* roofline: the dominant kernel's algorithmic bytes (or FLOPs) per launch over
+  its average launch time, against the MI355X peak;
+* cpu_baseline: the float64 oracle timed on a bounded sample of the same
+  workload on this host's cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tokens/s + sparse-attn HBM GB/s, 1 GPU, ctx 32k, top-k 2048"
+HBM_PEAK_GBPS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def algorithmic_work(wl):
+    """Bytes and FLOPs each stage must move/compute at minimum (per step)."""
+    cfg = wl.cfg
+    import oracle  # row layout only (visible lengths)
+    rows = oracle.row_layout(wl.seq_lens_k, wl.cu_seqlens_q)
+    vis = np.array([r.visible for r in rows], dtype=np.int64)
+    H, D, k = cfg.idx_heads, cfg.idx_dim, cfg.topk
+    esize = 1 if cfg.idx_kind == "fp8" else 4
+    key_bytes = D * esize + 4                       # 132 B for fp8 x 128 + fp32 scale
+    idx_bytes = int(vis.sum()) * (key_bytes + 4) + len(vis) * (H * D * esize + 4 * H)
+    idx_flops = int(vis.sum()) * 2 * H * D
+    topk_bytes = int(vis.sum()) * 4 + len(vis) * 4 * k
+    sel = np.minimum(vis, k)
+    Hm, Dl, Dr = cfg.mla_heads, cfg.d_latent, cfg.d_rope
+    msize = 2 if cfg.mla_kind == "bf16" else 4
+    row_bytes = (Dl + Dr) * msize
+    mla_bytes = int(sel.sum()) * row_bytes + len(vis) * (Hm * (Dl + Dr) * msize + Hm * Dl * msize
+                                                         + 4 * k + 4 * Hm)
+    mla_flops = int(sel.sum()) * Hm * (2 * (Dl + Dr) + 2 * Dl)
+    return {
+        "indexer": {"bytes": idx_bytes, "flops": idx_flops, "per_unit": f"{key_bytes + 4} B per visible key "
+                    f"(+{H * D * esize + 4 * H} B per row)", "units": int(vis.sum())},
+        "topk": {"bytes": topk_bytes, "flops": 0, "per_unit": f"4 B per visible score (+{4 * k} B per row)",
+                 "units": int(vis.sum())},
+        "sparse_mla": {"bytes": mla_bytes, "flops": mla_flops,
+                       "per_unit": f"{row_bytes} B per selected row (+{Hm * (Dl + Dr) * msize + Hm * Dl * msize + 4 * k + 4 * Hm} B per query row)",
+                       "units": int(sel.sum())},
+    }
+
+
+def cpu_baseline(wl, budget_s=12.0, max_rows=64):
+    """Oracle (float64 numpy) on whole rows of the workload until ~budget_s of CPU work."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    cfg = wl.cfg
+    vis = [r.visible for r in oracle.row_layout(wl.seq_lens_k, wl.cu_seqlens_q)]
+    t0 = time.perf_counter()
+    done = 0
+    for t in range(min(max_rows, wl.num_rows)):
+        logits = oracle.indexer_logits(wl.q_idx, wl.w, wl.index_cache, wl.block_table, wl.seq_lens_k,
+                                       wl.cu_seqlens_q, cfg.page_size, cfg.idx_kind, rows=[t])[t]
+        idx = oracle.topk_row(logits, vis[t], cfg.topk)
+        full_idx = np.full((wl.num_rows, cfg.topk), -1, dtype=np.int64)
+        full_idx[t] = idx
+        oracle.sparse_mla(wl.q_mla, wl.latent, full_idx, wl.block_table, wl.seq_lens_k, wl.cu_seqlens_q,
+                          cfg.page_size, cfg.d_latent, cfg.softmax_scale, cfg.mla_kind, rows=[t])
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {done} of {wl.num_rows} decode rows of the same workload, all three stages "
+                      f"(float64 numpy), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_b64_ragged")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the DSA step is not "
+              "sharded across GPUs in this library", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from dsa_workloads import CONFIGS, generate
+    from dsa_workloads.device import make_step
+
+    cfg = CONFIGS[args.workload]
+    t_gen = time.perf_counter()
+    wl = generate(cfg)
+    print(f"[bench] generated {cfg.name} in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+    step = make_step(wl, device="cuda:0")
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        e = ev[i]
+        e[0].record(stream)
+        step.indexer()
+        e[1].record(stream)
+        step.select()
+        e[2].record(stream)
+        step.attend()
+        e[3].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / K
+    stage_ms = {
+        "indexer": float(np.mean([e[0].elapsed_time(e[1]) for e in ev])),
+        "topk": float(np.mean([e[1].elapsed_time(e[2]) for e in ev])),
+        "sparse_mla": float(np.mean([e[2].elapsed_time(e[3]) for e in ev])),
+    }
+    print(f"[bench] timed {K} steps: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+
+    work = algorithmic_work(wl)
+    tokens_per_s = wl.num_rows / (ms_per_step * 1e-3)
+    kernels = {}
+    for name, w in work.items():
+        t_s = stage_ms[name] * 1e-3
+        gbps = w["bytes"] / t_s / 1e9
+        kernels[name] = {
+            "us": stage_ms[name] * 1e3,
+            "algorithmic_bytes": w["bytes"],
+            "algorithmic_flops": w["flops"],
+            "hbm_gbps": gbps,
+            "hbm_frac": gbps / HBM_PEAK_GBPS,
+            "per_unit": w["per_unit"],
+            "units": w["units"],
+        }
+        if w["flops"]:
+            peak = FP8_PEAK_TFLOPS if name == "indexer" and cfg.idx_kind == "fp8" else BF16_PEAK_TFLOPS
+            kernels[name]["tflops"] = w["flops"] / t_s / 1e12
+            kernels[name]["mfma_frac"] = kernels[name]["tflops"] / peak
+    dominant = max(stage_ms, key=stage_ms.get)
+    dk = kernels[dominant]
+    traffic = None
+    prof = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(prof):
+        try:
+            from sparse_mla_attention_dsa_amd.build import source_digest
+            rec = json.load(open(prof)).get(f"{cfg.name}:{dominant}")
+            if rec and rec.get("source_digest") == source_digest():
+                traffic = rec["bytes_per_launch"]
+        except Exception:
+            traffic = None
+    roofline = {"kernel": dominant, "bound": "hbm", "achieved": dk["hbm_gbps"], "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": dk["hbm_frac"], "traffic": traffic}
+
+    result = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "dtype_detail": "indexer fp8 e4m3 MFMA with fp32 accumulate; attention bf16 MFMA with fp32 softmax",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "description": cfg.note, "batch": cfg.batch,
+                   "ctx_total": int(wl.seq_lens_k.sum()), "ctx_max": wl.max_seq_len_k, "topk": cfg.topk,
+                   "page_size": cfg.page_size, "indexer": f"{cfg.idx_heads}x{cfg.idx_dim} {cfg.idx_kind}",
+                   "mla": f"{cfg.mla_heads} heads x {cfg.d_latent}+{cfg.d_rope} {cfg.mla_kind}"},
+        "sparse_attn_hbm_gbps": kernels["sparse_mla"]["hbm_gbps"],
+        "stages": kernels,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on a sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl, budget_s=args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

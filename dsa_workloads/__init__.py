@@ -11,20 +11,23 @@ stores each index key as fp8 plus one fp32 scale (`_store_index_k_cache`).
 Those quantizations happen before the step and are done here on the CPU with
 torch's float8_e4m3fn conversion so that both sides consume identical bytes.
 
-Draw order (numpy `default_rng(seed)`), fixed so the bytes are reproducible:
-1. context lengths (only for configs with a length range);
-2. page permutation of the pool; unused block-table slots point at one
-   extra poison page filled with NaN;
-3. index keys, standard normal [pages, P, D];
-4. index queries, standard normal [T, H, D];
-5. head weights, standard normal [T, H] / sqrt(H);
-6. latent cache, standard normal [pages, P, Dl + Dr];
-7. MLA queries, standard normal [T, Hm, Dl + Dr].
+Random streams (numpy PCG64), fixed so the bytes are reproducible:
+* `default_rng(seed)`: 1. context lengths (only for configs with a length
+  range); 2. the page permutation of the pool (unused block-table slots point
+  at one extra poison page filled with NaN);
+* every large array is drawn in float32 from its own streams
+  `default_rng([seed, array_id, chunk])`, one per chunk of the leading
+  dimension, so chunks can be filled in parallel and the bytes do not depend
+  on the number of threads: 3. index keys [pages, P, D] (array 1);
+  4. index queries [T, H, D] (2); 5. head weights [T, H] / sqrt(H) (3);
+  6. latent cache [pages, P, Dl + Dr] (4); 7. MLA queries [T, Hm, Dl + Dr] (5).
 Slots past a request's length inside its last page are NaN canaries.
 """
 
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 import math
+import os
 
 import numpy as np
 
@@ -123,13 +126,23 @@ def _to_e4m3fn_bytes(x32):
     return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
-def _normal_chunks(rng, shape, chunk_rows):
-    """standard_normal(shape) drawn in slices of the leading dim; the
-    generator's stream is the same as one call of the whole shape."""
-    out = np.empty(shape, dtype=np.float32)
-    for s in range(0, shape[0], chunk_rows):
+_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _fill(shape, seed, array_id, chunk_rows, dtype, convert=lambda x: x):
+    """Standard normal float32 values of `shape`, chunk i of the leading dim
+    drawn from default_rng([seed, array_id, i]) and passed through `convert`."""
+    out = np.empty(shape, dtype=dtype)
+    starts = list(range(0, shape[0], chunk_rows))
+
+    def work(i):
+        s = starts[i]
         e = min(shape[0], s + chunk_rows)
-        out[s:e] = rng.standard_normal((e - s,) + tuple(shape[1:]))
+        g = np.random.default_rng([seed, array_id, i])
+        out[s:e] = convert(g.standard_normal((e - s,) + tuple(shape[1:]), dtype=np.float32))
+
+    with ThreadPoolExecutor(_THREADS) as ex:
+        list(ex.map(work, range(len(starts))))
     return out
 
 
@@ -168,51 +181,55 @@ def generate(cfg, with_mla=True, with_indexer=True):
         block_table[b, :n] = pool[off:off + n]
         off += n
     num_pages = total + 1
-    # which (page, slot) pairs hold real tokens
-    live = np.zeros((num_pages, P), dtype=bool)
+    # slots that hold no token: the tail of each request's last page, and the
+    # whole poison page -> (page, first dead slot)
+    dead = [(poison, 0)]
     for b in range(B):
-        for p in range(n_pages[b]):
-            page = block_table[b, p]
-            cnt = min(P, int(lens[b]) - p * P)
-            if cnt > 0:
-                live[page, :cnt] = True
+        used = int(lens[b]) - (n_pages[b] - 1) * P
+        if used < P:
+            dead.append((int(block_table[b, n_pages[b] - 1]), max(0, used)))
+
+    def poison_slots(arr, value):
+        for page, first in dead:
+            arr[page, first:] = value
 
     H, D = cfg.idx_heads, cfg.idx_dim
     # 3. index keys (+ per-token scale)
     if with_indexer:
-        keys = _normal_chunks(rng, (total, P, D), 256)
+        keys = _fill((num_pages, P, D), cfg.seed, 1, 256, np.float32)
         if cfg.idx_kind == "fp8":
-            amax = np.abs(keys).max(axis=2)
-            sigma = (np.maximum(amax, np.float32(1e-30)) / np.float32(F8_MAX)).astype(np.float32)
-            codes = np.full((num_pages, P, D), NAN_F8, dtype=np.uint8)
-            for s in range(0, total, 4096):
-                e = min(total, s + 4096)
-                codes[s:e] = _to_e4m3fn_bytes(keys[s:e] / sigma[s:e, :, None])
-            sig_all = np.full((num_pages, P), np.nan, dtype=np.float32)
-            sig_all[:total] = sigma
-            # canaries: NaN keys and scales in dead slots and in the poison page
-            codes[~live] = NAN_F8
-            sig_all[~live] = np.nan
             page_bytes = P * D + 4 * P
             cache = np.empty((num_pages, page_bytes), dtype=np.uint8)
-            cache[:, :P * D] = codes.reshape(num_pages, P * D)
-            cache[:, P * D:] = sig_all.view(np.uint8).reshape(num_pages, 4 * P)
-            del codes
+            codes = cache[:, :P * D]
+            sig_all = cache[:, P * D:].view(np.float32)
+            bounds = list(range(0, num_pages, 1024))
+
+            def quant(s):
+                e = min(num_pages, s + 1024)
+                amax = np.abs(keys[s:e]).max(axis=2)
+                sig = (np.maximum(amax, np.float32(1e-30)) / np.float32(F8_MAX)).astype(np.float32)
+                sig_all[s:e] = sig
+                codes[s:e] = _to_e4m3fn_bytes(keys[s:e] / sig[:, :, None]).reshape(e - s, P * D)
+
+            with ThreadPoolExecutor(_THREADS) as ex:
+                list(ex.map(quant, bounds))
+            # canaries: NaN keys and scales in dead slots and in the poison page
+            for page, first in dead:
+                cache[page, first * D:P * D] = NAN_F8
+                sig_all[page, first:] = np.nan
         else:
             page_bytes = 4 * P * D + 4 * P
             cache = np.empty((num_pages, page_bytes), dtype=np.uint8)
-            kf = np.full((num_pages, P, D), np.nan, dtype=np.float32)
-            kf[:total] = keys
-            kf[~live] = np.nan
+            poison_slots(keys, np.nan)
             sf = np.ones((num_pages, P), dtype=np.float32)
-            sf[~live] = np.nan
-            cache[:, :4 * P * D] = kf.reshape(num_pages, -1).view(np.uint8)
+            poison_slots(sf, np.nan)
+            cache[:, :4 * P * D] = keys.reshape(num_pages, -1).view(np.uint8)
             cache[:, 4 * P * D:] = sf.view(np.uint8)
         del keys
 
         # 4. index queries, 5. head weights
-        qn = _normal_chunks(rng, (T, H, D), 1024)
-        wn = (rng.standard_normal((T, H)) / math.sqrt(H)).astype(np.float32)
+        qn = _fill((T, H, D), cfg.seed, 2, 1024, np.float32)
+        wn = (_fill((T, H), cfg.seed, 3, 1 << 30, np.float32) / np.float32(math.sqrt(H))).astype(np.float32)
         if cfg.idx_kind == "fp8":
             qb = _bf16_bits_to_f32(_to_bf16_bits(qn))           # q is bf16 before quantization
             amax = np.abs(qb).max(axis=2)
@@ -236,21 +253,13 @@ def generate(cfg, with_mla=True, with_indexer=True):
     Hm = cfg.mla_heads
     if with_mla:
         if cfg.mla_kind == "bf16":
-            latent = np.empty((num_pages, P, Dqk), dtype=np.uint16)
-            for s in range(0, total, 512):
-                e = min(total, s + 512)
-                latent[s:e] = _to_bf16_bits(rng.standard_normal((e - s, P, Dqk)).astype(np.float32))
-            latent[total:] = NAN_BF16
-            latent[~live] = NAN_BF16
-            q_mla = np.empty((T, Hm, Dqk), dtype=np.uint16)
-            for s in range(0, T, 256):
-                e = min(T, s + 256)
-                q_mla[s:e] = _to_bf16_bits(rng.standard_normal((e - s, Hm, Dqk)).astype(np.float32))
+            latent = _fill((num_pages, P, Dqk), cfg.seed, 4, 128, np.uint16, _to_bf16_bits)
+            poison_slots(latent, NAN_BF16)
+            q_mla = _fill((T, Hm, Dqk), cfg.seed, 5, 64, np.uint16, _to_bf16_bits)
         else:
-            latent = np.full((num_pages, P, Dqk), np.nan, dtype=np.float32)
-            latent[:total] = rng.standard_normal((total, P, Dqk)).astype(np.float32)
-            latent[~live] = np.nan
-            q_mla = rng.standard_normal((T, Hm, Dqk)).astype(np.float32)
+            latent = _fill((num_pages, P, Dqk), cfg.seed, 4, 128, np.float32)
+            poison_slots(latent, np.nan)
+            q_mla = _fill((T, Hm, Dqk), cfg.seed, 5, 64, np.float32)
     else:
         latent = np.zeros((num_pages, P, 0), dtype=np.uint16)
         q_mla = np.zeros((T, Hm, 0), dtype=np.uint16)

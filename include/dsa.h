@@ -1,0 +1,216 @@
+/*
+ * dsa.h - C ABI of the DeepSeek-Sparse-Attention (DSA) step on AMD gfx950.
+ *
+ * One DSA step of one MLA layer has three stages, each an entry point here:
+ *
+ *   dsa_indexer_logits  lightning-indexer scores over a paged fp8 index-K cache
+ *   dsa_topk            per-row top-k of those scores with causal/length masking
+ *   sparse_mla_decode   sparse MLA attention over the selected latent rows
+ *   sparse_mla_prefill  (decode: one query row per request; prefill: many)
+ *
+ * Sources: the SGLang "dsa_indexer.py" page (Indexer._get_topk_paged calls the
+ * paged fp8 MQA-logits kernel with q_fp8 [T,H,128], the 132-byte-per-token
+ * index cache, weights [T,H], seqlens and block tables, then topk_transform),
+ * the Ascend "sfa_v1.py" page (npu_lightning_indexer / npu_sparse_flash_attention
+ * take TND queries, a paged PA_BSND cache, block_table, cumulative query
+ * lengths and key lengths, sparse_count=2048, sparse_mode=3 i.e. causal), and
+ * the vLLM "mla/common.py" page (decode returns (out, lse); LSE merge of
+ * partial results with merge_attn_states).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers are DEVICE pointers unless the comment says "host". The dsa_batch_t
+ *   struct itself is read on the host during the call and may be freed after it.
+ * - Every call is asynchronous on `stream` (a hipStream_t; 0 = the null
+ *   stream), never synchronizes the host, allocates no memory, keeps no state
+ *   between calls and is safe to call from several threads. Calls contain no
+ *   host-device synchronization and no memset nodes, so they can be captured
+ *   into a HIP graph.
+ * - The caller owns every buffer. Inputs are read-only; outputs must not alias
+ *   inputs.
+ * - Arguments are validated on the host before anything is launched. On error
+ *   nothing is launched and a dsa_status_t other than DSA_OK is returned;
+ *   dsa_last_error() then gives a thread-local description.
+ * - Device-side contents (block-table entries, lengths, top-k indices) are
+ *   not validated on the host, but the kernels never read outside the buffers
+ *   the shapes describe: a page id outside [0, num_pages) or a position outside
+ *   the request's length is treated as absent (logit -inf, attention entry
+ *   skipped).
+ *
+ * Batch and causality
+ * -------------------
+ * Request b owns `seq_lens_k[b]` keys at logical positions [0, seq_lens_k[b]);
+ * position p lives in physical page block_table[b * max_pages_per_seq + p / P],
+ * slot p % P (both caches share page ids). Query rows are laid out "TND":
+ * with cu_seqlens_q == NULL there is one row per request (decode, row t =
+ * request t); otherwise request b owns rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1.
+ * Causality is bottom-right aligned (sparse_mode=3): the j-th of q_len_b rows
+ * of request b sees visible = seq_lens_k[b] - q_len_b + j + 1 keys, positions
+ * [0, visible). In decode every row sees its whole request.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *dsa_stream_t; /* identical to hipStream_t */
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, stride or count */
+  DSA_ERR_UNSUPPORTED = 2,      /* valid, but a shape/dtype this build has no kernel for */
+  DSA_ERR_WORKSPACE_TOO_SMALL = 3,
+  DSA_ERR_HIP = 4               /* the HIP runtime reported an error at launch */
+} dsa_status_t;
+
+typedef enum {
+  DSA_F32 = 0,
+  DSA_BF16 = 1,
+  DSA_FP8_E4M3 = 2 /* OCP E4M3 ("fn": no infinities, 0x7F/0xFF NaN, max 448) */
+} dsa_dtype_t;
+
+typedef enum {
+  DSA_OP_TOPK = 0,
+  DSA_OP_MLA_DECODE = 1,
+  DSA_OP_MLA_PREFILL = 2
+} dsa_op_t;
+
+typedef struct {
+  int32_t num_seqs;          /* B >= 0 */
+  int32_t num_rows;          /* T: query rows; must equal B when cu_seqlens_q == NULL */
+  int32_t page_size;         /* P: tokens per page, a positive multiple of 16 */
+  int32_t max_pages_per_seq; /* row stride of block_table, >= 1 */
+  int32_t num_pages;         /* pages in each cache pool; page ids outside [0, num_pages) are absent */
+  int32_t max_seq_len_k;     /* host: >= every seq_lens_k[b]; sizes grids, never read back */
+  int32_t max_seq_len_q;     /* host: >= every q_len_b (1 for decode) */
+  const int32_t *block_table;  /* [B, max_pages_per_seq] physical page ids */
+  const int32_t *seq_lens_k;   /* [B] keys in the cache, this step's tokens included */
+  const int32_t *cu_seqlens_q; /* [B+1] row prefix sums (cu[0] = 0, cu[B] = T), or NULL */
+} dsa_batch_t;
+
+/*
+ * dsa_indexer_logits - lightning-indexer scores (SGLang page,
+ * Indexer._get_topk_paged / forward_indexer):
+ *
+ *   logits[t, s] = sum_h w[t,h] * relu(sigma_s * (q[t,h,:] . k_s[:]))   for s < visible(t)
+ *
+ * q:        [T, H, D], q_dtype FP8_E4M3 with H = 64, D = 128, or F32 with
+ *           H <= 64, D <= 128 (any H, D in that range).
+ * w:        [T, H] fp32 head gates with the query's quantization scale (and any
+ *           head or softmax scale) already folded in.
+ * index_cache: paged keys. Page i starts at byte i * (P*D*esize + 4*P): P*D key
+ *           elements of k_dtype (token-major, D per token), then P fp32 scales
+ *           sigma. With P = 64, D = 128 and fp8 keys this is the 132 bytes per
+ *           token of the pages. k_dtype must equal q_dtype. sigma must be >= 0
+ *           (absmax-derived scales are); the kernel applies it after the head sum,
+ *           which equals the formula for sigma >= 0.
+ * logits:   [T, logits_row_stride] fp32, logits_row_stride >= max visible.
+ *           Columns >= visible(t) are left unwritten (the pages call their kernels
+ *           with clean_logits=False); a position whose page is absent gets -inf.
+ */
+dsa_status_t dsa_indexer_logits(const dsa_batch_t *batch,
+                                const void *q, dsa_dtype_t q_dtype,
+                                const float *w,
+                                const void *index_cache, dsa_dtype_t k_dtype,
+                                int32_t num_heads, int32_t head_dim,
+                                float *logits, int64_t logits_row_stride,
+                                dsa_stream_t stream);
+
+/*
+ * dsa_topk - per-row top-k selection (SGLang page: topk_transform after the
+ * logits; forward_indexer takes topk(min(topk, seq_len)) and pads with -1;
+ * _forward_cuda_k_only relies on rows of length <= k giving [0 .. len-1, -1 ...]).
+ *
+ * For each row t, with n = min(visible(t), logits_row_stride):
+ *   n <= k: topk_idx[t] = 0, 1, ..., n-1, then -1.
+ *   n >  k: the k positions s < n with the largest logits[t, s], in ascending
+ *           position order; among equal values at the k-th place the lower
+ *           positions are taken. Values are compared as floats with -0 == +0;
+ *           logits must not be NaN.
+ * topk_idx: [T, k] int32 logical positions. 1 <= k <= 4096.
+ * workspace: dsa_workspace_bytes(DSA_OP_TOPK, ...) bytes (currently 0; NULL ok).
+ */
+dsa_status_t dsa_topk(const dsa_batch_t *batch,
+                      const float *logits, int64_t logits_row_stride, int32_t k,
+                      int32_t *topk_idx,
+                      void *workspace, size_t workspace_bytes,
+                      dsa_stream_t stream);
+
+/*
+ * sparse_mla_decode / sparse_mla_prefill - sparse MLA attention over the
+ * selected latent rows (Ascend SFA page, npu_sparse_flash_attention with
+ * key = value = latent cache, the rope key passed separately, token-granular
+ * sparse indices and sparse_mode=3; vLLM MLA page: the decode path returns
+ * (attn_out, lse), and the cached row is the 512-d latent followed by the 64-d
+ * rope key). For each row t and head h, over the valid entries i of topk_idx[t]
+ * (entries < 0 or >= seq_lens_k[b] are skipped, so are absent pages):
+ *
+ *   C_i   = kv_cache row of position topk_idx[t, i]   (d_latent + d_rope values)
+ *   z_i   = softmax_scale * (q[t,h,:] . C_i)
+ *   out[t,h,:] = sum_i softmax(z)_i * C_i[:d_latent]
+ *   lse[t,h]   = log(sum_i exp(z_i))                  (natural log)
+ *
+ * A row with no valid entry gets out = 0 and lse = -inf. Duplicate entries are
+ * counted as many times as they appear. Entries should lie below the row's
+ * visible length; the call does not enforce causality itself.
+ *
+ * q:        [T, Hm, d_latent + d_rope] (absorbed no-rope part, then rope part)
+ * kv_cache: [num_pages, P, d_latent + d_rope]
+ * dtype:    BF16 with (Hm, d_latent, d_rope) = (128, 512, 64) or any Hm that is
+ *           a multiple of 64 with those dims; or F32 with Hm <= 128,
+ *           d_latent + d_rope <= 1024, d_latent <= 512.
+ * topk_idx: [T, k] int32, 1 <= k <= 4096.
+ * out:      [T, Hm, d_latent] in dtype.   lse: [T, Hm] fp32, may be NULL.
+ * workspace: at least dsa_workspace_bytes(DSA_OP_MLA_DECODE or _PREFILL, ...)
+ *           bytes of device memory (split-KV partial results); NULL if that is 0.
+ *
+ * sparse_mla_decode requires cu_seqlens_q == NULL (one row per request);
+ * sparse_mla_prefill requires cu_seqlens_q != NULL.
+ */
+dsa_status_t sparse_mla_decode(const dsa_batch_t *batch,
+                               const void *q, const void *kv_cache, dsa_dtype_t dtype,
+                               const int32_t *topk_idx, int32_t k,
+                               int32_t num_heads, int32_t d_latent, int32_t d_rope,
+                               float softmax_scale,
+                               void *out, float *lse,
+                               void *workspace, size_t workspace_bytes,
+                               dsa_stream_t stream);
+
+dsa_status_t sparse_mla_prefill(const dsa_batch_t *batch,
+                                const void *q, const void *kv_cache, dsa_dtype_t dtype,
+                                const int32_t *topk_idx, int32_t k,
+                                int32_t num_heads, int32_t d_latent, int32_t d_rope,
+                                float softmax_scale,
+                                void *out, float *lse,
+                                void *workspace, size_t workspace_bytes,
+                                dsa_stream_t stream);
+
+/*
+ * dsa_workspace_bytes - device workspace an op needs for this batch (host-only,
+ * launches nothing). Returns 0 for an op that needs none, and (size_t)-1 when
+ * the arguments are invalid (dsa_last_error() says why). `num_heads` and
+ * `d_latent` are the MLA ones; they are ignored for DSA_OP_TOPK. `dtype` is the
+ * MLA dtype.
+ */
+size_t dsa_workspace_bytes(dsa_op_t op, const dsa_batch_t *batch, int32_t k,
+                           int32_t num_heads, int32_t d_latent, dsa_dtype_t dtype);
+
+/* Static description of a status code. Never NULL. */
+const char *dsa_status_string(dsa_status_t status);
+
+/* Thread-local text of the last non-OK status returned on this thread ("" if none). */
+const char *dsa_last_error(void);
+
+/* Library version, "major.minor.patch". */
+const char *dsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H_ */

@@ -1,0 +1,71 @@
+// Device helpers shared by the DSA kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+
+// Row t of a batch -> (request b, index j of the row inside the request, rows of
+// the request). cu == nullptr means one row per request (decode).
+__device__ __forceinline__ void row_to_seq(int t, const int32_t* __restrict__ cu, int num_seqs,
+                                           int* b, int* j, int* q_len) {
+  if (cu == nullptr) {
+    *b = t; *j = 0; *q_len = 1;
+    return;
+  }
+  // largest b with cu[b] <= t (cu is non-decreasing; empty requests are skipped)
+  int lo = 0, hi = num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  *b = lo;
+  *j = t - cu[lo];
+  *q_len = cu[lo + 1] - cu[lo];
+}
+
+// Keys the row may see under bottom-right causal alignment, clamped to what the
+// block table and the caller's buffers can address.
+__device__ __forceinline__ int visible_keys(int seq_len_k, int q_len, int j, int cap) {
+  int v = seq_len_k - q_len + j + 1;
+  v = v < 0 ? 0 : v;
+  return v < cap ? v : cap;
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  const uint32_t r = u + 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(r >> 16);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// Order-preserving map of a float to an unsigned key: a < b  <=>  key(a) < key(b),
+// with -0 mapped onto +0 so that equal floats get equal keys.
+__device__ __forceinline__ uint32_t ordered_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
+  return __shfl_xor(v, mask, kWave);
+}
+
+}  // namespace dsa

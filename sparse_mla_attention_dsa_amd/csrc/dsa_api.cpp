@@ -1,0 +1,292 @@
+// C ABI of the DSA step: argument validation, dispatch to the kernel launchers,
+// workspace sizing and error reporting. Validation runs entirely on the host
+// before any HIP call, so invalid calls return without touching a device.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "dsa.h"
+#include "dsa_internal.h"
+
+using namespace dsa;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dsa_status_t fail(dsa_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+dsa_status_t ok() { return DSA_OK; }
+
+dsa_status_t from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Checks shared by every entry point; fills `bv` on success.
+dsa_status_t check_batch(const dsa_batch_t* batch, BatchView* bv) {
+  if (!batch) return fail(DSA_ERR_INVALID_ARGUMENT, "batch is NULL");
+  const dsa_batch_t& b = *batch;
+  if (b.num_seqs < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "num_seqs %d < 0", b.num_seqs);
+  if (b.num_rows < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "num_rows %d < 0", b.num_rows);
+  if (b.page_size <= 0 || b.page_size % 16 != 0)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "page_size %d is not a positive multiple of 16", b.page_size);
+  if (b.max_pages_per_seq < 1)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "max_pages_per_seq %d < 1", b.max_pages_per_seq);
+  if (b.num_pages < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "num_pages %d < 1", b.num_pages);
+  if ((int64_t)b.num_pages * b.page_size > INT32_MAX)
+    return fail(DSA_ERR_UNSUPPORTED, "num_pages * page_size exceeds 2^31 - 1 cache rows");
+  if ((int64_t)b.max_pages_per_seq * b.page_size > INT32_MAX)
+    return fail(DSA_ERR_UNSUPPORTED, "max_pages_per_seq * page_size exceeds 2^31 - 1 positions");
+  if (b.max_seq_len_k < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "max_seq_len_k %d < 0", b.max_seq_len_k);
+  if (b.max_seq_len_q < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "max_seq_len_q %d < 0", b.max_seq_len_q);
+  if (b.num_seqs > 0 && (!b.block_table || !b.seq_lens_k))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "block_table / seq_lens_k is NULL");
+  if (b.cu_seqlens_q == nullptr) {
+    if (b.num_rows != b.num_seqs)
+      return fail(DSA_ERR_INVALID_ARGUMENT, "num_rows %d != num_seqs %d with cu_seqlens_q == NULL",
+                  b.num_rows, b.num_seqs);
+    if (b.num_rows > 0 && b.max_seq_len_q > 1)
+      return fail(DSA_ERR_INVALID_ARGUMENT, "max_seq_len_q %d > 1 with cu_seqlens_q == NULL", b.max_seq_len_q);
+  } else {
+    if (b.num_seqs < 1 && b.num_rows > 0)
+      return fail(DSA_ERR_INVALID_ARGUMENT, "rows without requests");
+    if (b.num_rows > 0 && b.max_seq_len_q < 1)
+      return fail(DSA_ERR_INVALID_ARGUMENT, "max_seq_len_q %d < 1 with rows present", b.max_seq_len_q);
+  }
+  bv->num_seqs = b.num_seqs;
+  bv->num_rows = b.num_rows;
+  bv->page_size = b.page_size;
+  bv->max_pages_per_seq = b.max_pages_per_seq;
+  bv->num_pages = b.num_pages;
+  bv->max_seq_len_k = b.max_seq_len_k;
+  bv->max_seq_len_q = b.max_seq_len_q;
+  bv->block_table = b.block_table;
+  bv->seq_lens_k = b.seq_lens_k;
+  bv->cu_seqlens_q = b.cu_seqlens_q;
+  return ok();
+}
+
+struct MlaPlan {
+  bool bf16;
+  int splits;
+  int entries_per_split;
+  size_t workspace;
+};
+
+dsa_status_t plan_mla(const BatchView& bv, int32_t k, int32_t num_heads, int32_t d_latent,
+                      int32_t d_rope, dsa_dtype_t dtype, MlaPlan* plan) {
+  if (k < 1 || k > kTopkMaxK) return fail(DSA_ERR_INVALID_ARGUMENT, "k %d outside [1, %d]", k, kTopkMaxK);
+  if (num_heads < 1 || d_latent < 1 || d_rope < 0)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "num_heads %d, d_latent %d, d_rope %d", num_heads, d_latent, d_rope);
+  if (dtype == DSA_BF16) {
+    if (d_latent != kMlaDl || d_rope != kMlaDr || num_heads % kMlaHeadsPerGroup != 0)
+      return fail(DSA_ERR_UNSUPPORTED,
+                  "bf16 sparse MLA needs d_latent 512, d_rope 64 and a multiple of 64 heads "
+                  "(got %d, %d, %d)", d_latent, d_rope, num_heads);
+    plan->bf16 = true;
+    plan->splits = mla_bf16_splits(bv.num_rows, k, num_heads);
+    plan->entries_per_split = mla_entries_per_split(k, plan->splits);
+    plan->workspace = 0;
+    if (plan->splits > 1) {
+      const size_t parts = (size_t)bv.num_rows * plan->splits * num_heads;
+      plan->workspace = parts * (size_t)d_latent * sizeof(float) + parts * sizeof(float);
+    }
+    return ok();
+  }
+  if (dtype == DSA_F32) {
+    if (num_heads > 128 || d_latent > 512 || d_latent + d_rope > 1024)
+      return fail(DSA_ERR_UNSUPPORTED, "f32 sparse MLA supports num_heads <= 128, d_latent <= 512, "
+                  "d_latent + d_rope <= 1024 (got %d, %d, %d)", num_heads, d_latent, d_rope);
+    plan->bf16 = false;
+    plan->splits = 1;
+    plan->entries_per_split = k;
+    plan->workspace = 0;
+    return ok();
+  }
+  return fail(DSA_ERR_UNSUPPORTED, "sparse MLA dtype %d (BF16 or F32 only)", (int)dtype);
+}
+
+dsa_status_t run_mla(const dsa_batch_t* batch, bool decode, const void* q, const void* kv_cache,
+                     dsa_dtype_t dtype, const int32_t* topk_idx, int32_t k, int32_t num_heads,
+                     int32_t d_latent, int32_t d_rope, float softmax_scale, void* out, float* lse,
+                     void* workspace, size_t workspace_bytes, dsa_stream_t stream) {
+  BatchView bv;
+  dsa_status_t st = check_batch(batch, &bv);
+  if (st != DSA_OK) return st;
+  if (decode && bv.cu_seqlens_q != nullptr)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "sparse_mla_decode needs cu_seqlens_q == NULL");
+  if (!decode && bv.cu_seqlens_q == nullptr)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "sparse_mla_prefill needs cu_seqlens_q");
+  MlaPlan plan;
+  st = plan_mla(bv, k, num_heads, d_latent, d_rope, dtype, &plan);
+  if (st != DSA_OK) return st;
+  if (!(softmax_scale == softmax_scale) || softmax_scale == INFINITY || softmax_scale == -INFINITY)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "softmax_scale is not finite");
+  if (bv.num_rows > 0 && (!q || !kv_cache || !topk_idx || !out))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "q / kv_cache / topk_idx / out is NULL");
+  if (workspace_bytes < plan.workspace)
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, plan.workspace);
+  if (plan.workspace > 0 && !workspace)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (bv.num_rows == 0) return ok();
+
+  MlaParams p;
+  p.batch = bv;
+  p.q = q;
+  p.kv = kv_cache;
+  p.topk_idx = topk_idx;
+  p.k = k;
+  p.heads = num_heads;
+  p.d_latent = d_latent;
+  p.d_rope = d_rope;
+  p.softmax_scale = softmax_scale;
+  p.out = out;
+  p.lse = lse;
+  p.splits = plan.splits;
+  p.entries_per_split = plan.entries_per_split;
+  p.part_o = nullptr;
+  p.part_lse = nullptr;
+  if (plan.splits > 1) {
+    const size_t parts = (size_t)bv.num_rows * plan.splits * num_heads;
+    p.part_o = static_cast<float*>(workspace);
+    p.part_lse = static_cast<float*>(workspace) + parts * (size_t)d_latent;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return from_hip(plan.bf16 ? launch_mla_bf16(p, s) : launch_mla_f32(p, s), "sparse MLA launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status_t dsa_indexer_logits(const dsa_batch_t* batch, const void* q, dsa_dtype_t q_dtype,
+                                const float* w, const void* index_cache, dsa_dtype_t k_dtype,
+                                int32_t num_heads, int32_t head_dim, float* logits,
+                                int64_t logits_row_stride, dsa_stream_t stream) {
+  BatchView bv;
+  dsa_status_t st = check_batch(batch, &bv);
+  if (st != DSA_OK) return st;
+  if (q_dtype != k_dtype)
+    return fail(DSA_ERR_UNSUPPORTED, "q_dtype %d != k_dtype %d", (int)q_dtype, (int)k_dtype);
+  if (num_heads < 1 || head_dim < 1)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "num_heads %d / head_dim %d < 1", num_heads, head_dim);
+  if (q_dtype == DSA_FP8_E4M3) {
+    if (num_heads != kIdxHeads || head_dim != kIdxDim)
+      return fail(DSA_ERR_UNSUPPORTED, "fp8 indexer needs 64 heads x 128 (got %d x %d)", num_heads, head_dim);
+  } else if (q_dtype == DSA_F32) {
+    if (num_heads > kIdxHeads || head_dim > kIdxDim)
+      return fail(DSA_ERR_UNSUPPORTED, "f32 indexer supports up to 64 heads x 128 (got %d x %d)",
+                  num_heads, head_dim);
+  } else {
+    return fail(DSA_ERR_UNSUPPORTED, "indexer dtype %d (FP8_E4M3 or F32 only)", (int)q_dtype);
+  }
+  if (logits_row_stride < (int64_t)bv.max_seq_len_k || logits_row_stride < 1)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "logits_row_stride %lld < max_seq_len_k %d",
+                (long long)logits_row_stride, bv.max_seq_len_k);
+  if (bv.num_rows > 0 && (!q || !w || !index_cache || !logits))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "q / w / index_cache / logits is NULL");
+  if (bv.num_rows == 0 || bv.max_seq_len_k == 0) return ok();
+  IndexerParams p;
+  p.batch = bv;
+  p.q = q;
+  p.w = w;
+  p.cache = static_cast<const uint8_t*>(index_cache);
+  const int64_t esize = q_dtype == DSA_FP8_E4M3 ? 1 : 4;
+  p.page_bytes = (int64_t)bv.page_size * head_dim * esize + 4LL * bv.page_size;
+  p.heads = num_heads;
+  p.dim = head_dim;
+  p.logits = logits;
+  p.stride = logits_row_stride;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return from_hip(q_dtype == DSA_FP8_E4M3 ? launch_indexer_fp8(p, s) : launch_indexer_f32(p, s),
+                  "indexer launch");
+}
+
+dsa_status_t dsa_topk(const dsa_batch_t* batch, const float* logits, int64_t logits_row_stride,
+                      int32_t k, int32_t* topk_idx, void* workspace, size_t workspace_bytes,
+                      dsa_stream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  BatchView bv;
+  dsa_status_t st = check_batch(batch, &bv);
+  if (st != DSA_OK) return st;
+  if (k < 1 || k > kTopkMaxK) return fail(DSA_ERR_INVALID_ARGUMENT, "k %d outside [1, %d]", k, kTopkMaxK);
+  if (logits_row_stride < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "logits_row_stride < 1");
+  if (bv.num_rows > 0 && (!logits || !topk_idx))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "logits / topk_idx is NULL");
+  if (bv.num_rows == 0) return ok();
+  TopkParams p;
+  p.batch = bv;
+  p.logits = logits;
+  p.stride = logits_row_stride;
+  p.k = k;
+  p.topk_idx = topk_idx;
+  return from_hip(launch_topk(p, reinterpret_cast<hipStream_t>(stream)), "top-k launch");
+}
+
+dsa_status_t sparse_mla_decode(const dsa_batch_t* batch, const void* q, const void* kv_cache,
+                               dsa_dtype_t dtype, const int32_t* topk_idx, int32_t k,
+                               int32_t num_heads, int32_t d_latent, int32_t d_rope, float softmax_scale,
+                               void* out, float* lse, void* workspace, size_t workspace_bytes,
+                               dsa_stream_t stream) {
+  return run_mla(batch, true, q, kv_cache, dtype, topk_idx, k, num_heads, d_latent, d_rope,
+                 softmax_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+dsa_status_t sparse_mla_prefill(const dsa_batch_t* batch, const void* q, const void* kv_cache,
+                                dsa_dtype_t dtype, const int32_t* topk_idx, int32_t k,
+                                int32_t num_heads, int32_t d_latent, int32_t d_rope, float softmax_scale,
+                                void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                dsa_stream_t stream) {
+  return run_mla(batch, false, q, kv_cache, dtype, topk_idx, k, num_heads, d_latent, d_rope,
+                 softmax_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+size_t dsa_workspace_bytes(dsa_op_t op, const dsa_batch_t* batch, int32_t k, int32_t num_heads,
+                           int32_t d_latent, dsa_dtype_t dtype) {
+  BatchView bv;
+  if (check_batch(batch, &bv) != DSA_OK) return (size_t)-1;
+  if (op == DSA_OP_TOPK) {
+    if (k < 1 || k > kTopkMaxK) {
+      fail(DSA_ERR_INVALID_ARGUMENT, "k %d outside [1, %d]", k, kTopkMaxK);
+      return (size_t)-1;
+    }
+    return 0;
+  }
+  if (op == DSA_OP_MLA_DECODE || op == DSA_OP_MLA_PREFILL) {
+    MlaPlan plan;
+    const int d_rope = dtype == DSA_BF16 ? kMlaDr : 0;
+    if (plan_mla(bv, k, num_heads, d_latent, d_rope, dtype, &plan) != DSA_OK) return (size_t)-1;
+    return plan.workspace;
+  }
+  fail(DSA_ERR_INVALID_ARGUMENT, "unknown op %d", (int)op);
+  return (size_t)-1;
+}
+
+const char* dsa_status_string(dsa_status_t status) {
+  switch (status) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case DSA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case DSA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case DSA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* dsa_last_error(void) { return g_last_error.c_str(); }
+
+const char* dsa_version(void) { return "0.1.0"; }
+
+}  // extern "C"

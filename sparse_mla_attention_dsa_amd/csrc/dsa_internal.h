@@ -1,0 +1,84 @@
+// Launch parameters shared between the host API layer and the kernel files.
+// The host layer validates every field before a launcher is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+struct BatchView {
+  int32_t num_seqs;
+  int32_t num_rows;
+  int32_t page_size;
+  int32_t max_pages_per_seq;
+  int32_t num_pages;
+  int32_t max_seq_len_k;
+  int32_t max_seq_len_q;
+  const int32_t* block_table;
+  const int32_t* seq_lens_k;
+  const int32_t* cu_seqlens_q;  // nullptr = decode
+};
+
+struct IndexerParams {
+  BatchView batch;
+  const void* q;          // [T, H, D]
+  const float* w;         // [T, H]
+  const uint8_t* cache;   // pages of page_bytes
+  int64_t page_bytes;
+  int32_t heads;
+  int32_t dim;
+  float* logits;
+  int64_t stride;
+};
+
+struct TopkParams {
+  BatchView batch;
+  const float* logits;
+  int64_t stride;
+  int32_t k;
+  int32_t* topk_idx;      // [T, k]
+};
+
+struct MlaParams {
+  BatchView batch;
+  const void* q;          // [T, Hm, Dqk]
+  const void* kv;         // [num_pages, P, Dqk]
+  const int32_t* topk_idx;
+  int32_t k;
+  int32_t heads;
+  int32_t d_latent;
+  int32_t d_rope;
+  float softmax_scale;
+  void* out;              // [T, Hm, Dl]
+  float* lse;             // [T, Hm] or nullptr
+  // split-KV partials (splits > 1): [T, splits, Hm, Dl] fp32 and [T, splits, Hm]
+  float* part_o;
+  float* part_lse;
+  int32_t splits;
+  int32_t entries_per_split;  // multiple of the tile height
+};
+
+// Shape constants of the MFMA paths.
+constexpr int kIdxHeads = 64;
+constexpr int kIdxDim = 128;
+constexpr int kMlaHeadsPerGroup = 64;
+constexpr int kMlaDl = 512;
+constexpr int kMlaDr = 64;
+constexpr int kMlaDqk = kMlaDl + kMlaDr;
+constexpr int kMlaTile = 32;
+constexpr int kMlaMaxEntriesPerBlock = 2048;
+constexpr int kTopkMaxK = 4096;
+
+// Split-KV policy for the bf16 kernel: enough work-groups to cover the chip
+// while keeping every split at least a few tiles long.
+int mla_bf16_splits(int num_rows, int k, int heads);
+int mla_entries_per_split(int k, int splits);
+
+hipError_t launch_indexer_fp8(const IndexerParams& p, hipStream_t s);
+hipError_t launch_indexer_f32(const IndexerParams& p, hipStream_t s);
+hipError_t launch_topk(const TopkParams& p, hipStream_t s);
+hipError_t launch_mla_bf16(const MlaParams& p, hipStream_t s);
+hipError_t launch_mla_f32(const MlaParams& p, hipStream_t s);
+
+}  // namespace dsa

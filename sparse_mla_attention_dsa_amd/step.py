@@ -1,0 +1,52 @@
+"""One DSA step of one layer on one stream: indexer logits -> top-k -> sparse MLA.
+
+Allocates the intermediate buffers once (logits, indices, output, lse,
+workspace) and replays the three library calls. Allocation happens here, in
+the constructor; `run()` itself allocates nothing.
+"""
+import torch
+
+from . import (DSA_BF16, DSA_F32, DSA_OP_MLA_DECODE, DSA_OP_MLA_PREFILL, dsa_indexer_logits,
+               dsa_topk, dsa_workspace_bytes, make_batch, sparse_mla_decode, sparse_mla_prefill)
+
+
+class DsaStep:
+    def __init__(self, *, block_table, seq_lens_k, cu_seqlens_q, page_size, num_pages,
+                 max_seq_len_k, max_seq_len_q, num_rows, q_idx, w, index_cache, q_mla, kv_cache,
+                 topk, softmax_scale, d_latent):
+        self.prefill = cu_seqlens_q is not None
+        self.batch = make_batch(block_table, seq_lens_k, cu_seqlens_q, page_size=page_size,
+                                num_pages=num_pages, max_seq_len_k=max_seq_len_k,
+                                max_seq_len_q=max_seq_len_q, num_rows=num_rows)
+        dev = q_mla.device
+        self.q_idx, self.w, self.index_cache = q_idx, w, index_cache
+        self.q_mla, self.kv_cache = q_mla, kv_cache
+        self.topk, self.softmax_scale, self.d_latent = int(topk), float(softmax_scale), int(d_latent)
+        T, Hm = num_rows, int(q_mla.shape[1])
+        stride = max(1, (max_seq_len_k + 3) // 4 * 4)
+        self.logits = torch.empty((T, stride), dtype=torch.float32, device=dev)
+        self.topk_idx = torch.empty((T, self.topk), dtype=torch.int32, device=dev)
+        out_dtype = torch.float32 if q_mla.dtype == torch.float32 else torch.bfloat16
+        self.out = torch.empty((T, Hm, self.d_latent), dtype=out_dtype, device=dev)
+        self.lse = torch.empty((T, Hm), dtype=torch.float32, device=dev)
+        mla_dtype = DSA_F32 if q_mla.dtype == torch.float32 else DSA_BF16
+        op = DSA_OP_MLA_PREFILL if self.prefill else DSA_OP_MLA_DECODE
+        nbytes = dsa_workspace_bytes(op, self.batch, self.topk, Hm, self.d_latent, mla_dtype)
+        self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev) if nbytes else None
+
+    def indexer(self, stream=None):
+        dsa_indexer_logits(self.batch, self.q_idx, self.w, self.index_cache, self.logits, stream=stream)
+
+    def select(self, stream=None):
+        dsa_topk(self.batch, self.logits, self.topk, self.topk_idx, stream=stream)
+
+    def attend(self, stream=None, topk_idx=None):
+        fn = sparse_mla_prefill if self.prefill else sparse_mla_decode
+        idx = self.topk_idx if topk_idx is None else topk_idx
+        fn(self.batch, self.q_mla, self.kv_cache, idx, self.softmax_scale, self.out, self.lse,
+           self.workspace, d_latent=self.d_latent, stream=stream)
+
+    def run(self, stream=None):
+        self.indexer(stream)
+        self.select(stream)
+        self.attend(stream)

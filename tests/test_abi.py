@@ -1,0 +1,173 @@
+"""The C ABI on the host: the library loads, exports every symbol declared in
+include/dsa.h, and rejects invalid arguments before touching a device.
+None of these calls launches a kernel (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparse_mla_attention_dsa_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(dsa.library_path()):
+        from sparse_mla_attention_dsa_amd.build import build
+        build()
+    return dsa.lib()
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "dsa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(\w+)\s*\([^;]*\)\s*;", text)) - {"if", "while"})
+
+
+def test_every_declared_symbol_is_exported(L):
+    declared = _declared()
+    assert set(declared) == set(dsa.EXPORTED_SYMBOLS), declared
+    out = subprocess.run(["nm", "-D", "--defined-only", dsa.library_path()], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared:
+        assert name in exported, name
+        assert hasattr(L, name)
+
+
+def test_version_and_status_strings(L):
+    assert re.fullmatch(r"\d+\.\d+\.\d+", dsa.dsa_version())
+    for st in range(5):
+        assert L.dsa_status_string(st)
+    assert L.dsa_status_string(99) == b"unknown status"
+
+
+class FakeTensor:
+    """A host-side stand-in with a data_ptr and strides; never dereferenced."""
+
+    def __init__(self, shape, dtype=None, ptr=0x1000):
+        self.shape = shape
+        self.dtype = dtype
+        self._ptr = ptr
+
+    def data_ptr(self):
+        return self._ptr
+
+    def stride(self, i):
+        s = 1
+        for d in self.shape[i + 1:]:
+            s *= d
+        return s
+
+
+def _batch(**kw):
+    args = dict(num_seqs=1, num_rows=1, page_size=64, max_pages_per_seq=4, num_pages=8,
+                max_seq_len_k=256, max_seq_len_q=1, block_table=0x2000, seq_lens_k=0x3000,
+                cu_seqlens_q=None)
+    args.update(kw)
+    return dsa.DsaBatch(**args)
+
+
+def _idx(L, batch, k=2048, stride=256):
+    return L.dsa_topk(ctypes.byref(batch), ctypes.c_void_p(0x4000), stride, k,
+                      ctypes.c_void_p(0x5000), None, 0, None)
+
+
+@pytest.mark.parametrize("field,value", [
+    ("page_size", 0), ("page_size", 24), ("page_size", -16), ("max_pages_per_seq", 0),
+    ("num_pages", 0), ("num_seqs", -1), ("num_rows", 2), ("max_seq_len_k", -5),
+    ("block_table", None), ("seq_lens_k", None), ("max_seq_len_q", 3),
+])
+def test_topk_rejects_bad_batches(L, field, value):
+    assert _idx(L, _batch(**{field: value})) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert L.dsa_last_error()
+
+
+@pytest.mark.parametrize("k", [0, -1, 4097])
+def test_topk_rejects_bad_k(L, k):
+    assert _idx(L, _batch(), k=k) == dsa.DSA_ERR_INVALID_ARGUMENT
+
+
+def test_null_batch(L):
+    assert L.dsa_topk(None, None, 1, 1, None, None, 0, None) == dsa.DSA_ERR_INVALID_ARGUMENT
+
+
+def test_huge_pool_is_unsupported(L):
+    assert _idx(L, _batch(num_pages=2 ** 30)) == dsa.DSA_ERR_UNSUPPORTED
+
+
+def test_empty_batch_is_ok_without_launch(L):
+    b = _batch(num_seqs=0, num_rows=0, block_table=None, seq_lens_k=None)
+    assert _idx(L, b) == dsa.DSA_OK
+
+
+def _logits(L, batch, qd=dsa.DSA_FP8_E4M3, kd=dsa.DSA_FP8_E4M3, H=64, D=128, stride=256, nullq=False):
+    return L.dsa_indexer_logits(ctypes.byref(batch), None if nullq else ctypes.c_void_p(0x100), qd,
+                                ctypes.c_void_p(0x200), ctypes.c_void_p(0x300), kd, H, D,
+                                ctypes.c_void_p(0x400), stride, None)
+
+
+def test_indexer_validation(L):
+    b = _batch()
+    assert _logits(L, b, H=32) == dsa.DSA_ERR_UNSUPPORTED
+    assert _logits(L, b, D=64) == dsa.DSA_ERR_UNSUPPORTED
+    assert _logits(L, b, kd=dsa.DSA_F32) == dsa.DSA_ERR_UNSUPPORTED
+    assert _logits(L, b, qd=dsa.DSA_BF16, kd=dsa.DSA_BF16) == dsa.DSA_ERR_UNSUPPORTED
+    assert _logits(L, b, qd=dsa.DSA_F32, kd=dsa.DSA_F32, H=65, D=8) == dsa.DSA_ERR_UNSUPPORTED
+    assert _logits(L, b, stride=255) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert _logits(L, b, nullq=True) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert _logits(L, b, H=0) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert _logits(L, _batch(num_rows=0, num_seqs=0)) == dsa.DSA_OK
+
+
+def _mla(L, batch, decode=True, dtype=dsa.DSA_BF16, H=128, Dl=512, Dr=64, k=2048, ws=None, wsb=0,
+         scale=0.07, nullout=False):
+    fn = L.sparse_mla_decode if decode else L.sparse_mla_prefill
+    return fn(ctypes.byref(batch), ctypes.c_void_p(0x10), ctypes.c_void_p(0x20), dtype,
+              ctypes.c_void_p(0x30), k, H, Dl, Dr, scale, None if nullout else ctypes.c_void_p(0x40),
+              None, ws, wsb, None)
+
+
+def test_mla_validation(L):
+    dec = _batch(num_seqs=64, num_rows=64)
+    need = L.dsa_workspace_bytes(dsa.DSA_OP_MLA_DECODE, ctypes.byref(dec), 2048, 128, 512, dsa.DSA_BF16)
+    assert need > 0                                         # split-KV partials for a 64-row decode
+    assert _mla(L, dec, ws=None, wsb=0) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
+    assert _mla(L, dec, ws=None, wsb=need) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert _mla(L, dec, H=96, ws=ctypes.c_void_p(0x50), wsb=need) == dsa.DSA_ERR_UNSUPPORTED
+    assert _mla(L, dec, Dl=256, ws=ctypes.c_void_p(0x50), wsb=need) == dsa.DSA_ERR_UNSUPPORTED
+    assert _mla(L, dec, dtype=dsa.DSA_FP8_E4M3) == dsa.DSA_ERR_UNSUPPORTED
+    assert _mla(L, dec, k=0) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert _mla(L, dec, scale=float("nan")) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert _mla(L, dec, nullout=True, ws=ctypes.c_void_p(0x50), wsb=need) == dsa.DSA_ERR_INVALID_ARGUMENT
+    # decode needs cu_seqlens_q == NULL, prefill needs it
+    pre = _batch(num_seqs=1, num_rows=4096, max_seq_len_q=4096, cu_seqlens_q=0x6000)
+    assert _mla(L, pre, decode=True) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert _mla(L, dec, decode=False) == dsa.DSA_ERR_INVALID_ARGUMENT
+    # a long prefill needs no partials
+    assert L.dsa_workspace_bytes(dsa.DSA_OP_MLA_PREFILL, ctypes.byref(pre), 2048, 128, 512, dsa.DSA_BF16) == 0
+    assert _mla(L, dsa.DsaBatch(**{**{f: getattr(pre, f) for f, _ in dsa.DsaBatch._fields_},
+                                   "num_rows": 0, "num_seqs": 1}), decode=False) == dsa.DSA_OK
+
+
+def test_workspace_bytes_errors(L):
+    b = _batch()
+    assert L.dsa_workspace_bytes(7, ctypes.byref(b), 16, 128, 512, dsa.DSA_BF16) == ctypes.c_size_t(-1).value
+    assert L.dsa_workspace_bytes(dsa.DSA_OP_TOPK, ctypes.byref(b), 0, 0, 0, 0) == ctypes.c_size_t(-1).value
+    assert L.dsa_workspace_bytes(dsa.DSA_OP_TOPK, ctypes.byref(b), 16, 0, 0, 0) == 0
+    with pytest.raises(dsa.DsaError):
+        dsa.dsa_workspace_bytes(dsa.DSA_OP_TOPK, dsa.Batch(b, ()), 0, 0, 0, 0)
+
+
+def test_python_binding_raises_on_errors(L):
+    bt = FakeTensor((1, 4))
+    sl = FakeTensor((1,))
+    batch = dsa.make_batch(bt, sl, page_size=24, num_pages=4, max_seq_len_k=10)
+    logits = FakeTensor((1, 16))
+    idx = FakeTensor((1, 8))
+    with pytest.raises(dsa.DsaError) as e:
+        dsa.dsa_topk(batch, logits, 8, idx, stream=0)
+    assert e.value.status == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert "page_size" in str(e.value)

@@ -1,0 +1,111 @@
+"""GPU parity: the HIP library (through its C ABI) against the float64 oracle.
+
+Small workloads are compared element by element; the full-size workloads are
+compared on sampled rows the oracle computes one at a time, in the same launch
+configuration the benchmark times.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from dsa_workloads import CONFIGS, generate, small_config  # noqa: E402
+from tests import parity  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _run(cfg):
+    _need_gpu()
+    from dsa_workloads.device import make_step
+    print(f"\n[parity] {cfg.name}: generating", flush=True)
+    wl = generate(cfg)
+    step = make_step(wl)
+    print(f"[parity] {cfg.name}: running T={wl.num_rows} max_len={wl.max_seq_len_k}", flush=True)
+    step.run()
+    torch.cuda.synchronize()
+    host = {
+        "logits": step.logits.cpu().numpy(),
+        "topk": step.topk_idx.cpu().numpy(),
+        "out": step.out.float().cpu().numpy(),
+        "lse": step.lse.cpu().numpy(),
+    }
+    return wl, step, host
+
+
+def _full_check(cfg, rows=None):
+    wl, step, h = _run(cfg)
+    rows = list(range(wl.num_rows)) if rows is None else rows
+    ref, worst_l = parity.check_logits(h["logits"], wl, rows)
+    vis = parity.visible_of(wl)
+    parity.check_topk_exact(h["topk"], h["logits"], vis, cfg.topk, rows)
+    n_near = sum(parity.check_topk_near_ties(h["topk"][t], ref[t], vis[t], cfg.topk) for t in rows)
+    worst_o = parity.check_attention(h["out"], h["lse"], wl, h["topk"], rows, fp32=cfg.mla_kind == "f32")
+    print(f"[parity] {cfg.name}: rows {len(rows)} logits err/bound {worst_l:.3f} "
+          f"near-tie swaps {n_near} attention err/bound {worst_o:.3f}", flush=True)
+    return wl, step, h
+
+
+SMALL = [
+    CONFIGS["tiny"],
+    small_config("dec3_p64", seed=101, lens=[100, 2100, 5000]),
+    small_config("dec2_p16_k256", seed=102, lens=[700, 1500], page_size=16, topk=256),
+    small_config("dec4_ragged_tail", seed=103, lens=[2049, 3333, 64, 4097]),
+    small_config("pre2_p64", seed=104, lens=[300, 2500], q_lens=[37, 64]),
+    small_config("pre2_k128", seed=105, lens=[400, 1000], q_lens=[50, 21], topk=128),
+    small_config("pre1_k4096", seed=106, lens=[5000], q_lens=[40], topk=4096),
+    small_config("dec_f32", seed=107, lens=[90, 300], page_size=16, topk=64, idx_kind="f32", mla_kind="f32"),
+    small_config("pre_f32", seed=108, lens=[120, 77], q_lens=[9, 13], page_size=16, topk=32,
+                 idx_kind="f32", mla_kind="f32"),
+    small_config("dec_k1", seed=109, lens=[500, 33], topk=1),
+    small_config("dec_empty_row", seed=110, lens=[0, 700], page_size=64, topk=256),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=[c.name for c in SMALL])
+def test_small_workloads_match_oracle(cfg):
+    _full_check(cfg)
+
+
+def test_full_single_decode_8k():
+    _full_check(CONFIGS["decode_b1_8k"])
+
+
+def test_full_ragged_batch64_sampled():
+    cfg = CONFIGS["decode_b64_ragged"]
+    wl = generate(cfg, with_mla=False)
+    lens = wl.seq_lens_k
+    rows = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 17})
+    _full_check(cfg, rows=rows)
+
+
+def test_full_long_context_128k_sampled():
+    _full_check(CONFIGS["decode_b8_128k"], rows=[0, 5])
+
+
+def test_full_prefill_sampled():
+    _full_check(CONFIGS["prefill_4k_on_16k"], rows=[0, 1, 2047, 4094, 4095])
+
+
+def test_empty_batch_launches_nothing():
+    _need_gpu()
+    import sparse_mla_attention_dsa_amd as dsa
+    dev = "cuda"
+    bt = torch.zeros((1, 1), dtype=torch.int32, device=dev)
+    sl = torch.zeros((0,), dtype=torch.int32, device=dev)
+    batch = dsa.make_batch(bt, sl, page_size=64, num_pages=1, max_seq_len_k=0, max_seq_len_q=1)
+    logits = torch.empty((0, 1), dtype=torch.float32, device=dev)
+    idx = torch.empty((0, 16), dtype=torch.int32, device=dev)
+    dsa.dsa_topk(batch, logits, 16, idx)
+    torch.cuda.synchronize()
+
+
+if __name__ == "__main__":
+    sys.exit(pytest.main([__file__, "-v"]))
