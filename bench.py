@@ -61,7 +61,7 @@ def algorithmic_work(wl):
     }
 
 
-def cpu_baseline(wl, budget_s=12.0, max_rows=64):
+def cpu_baseline(wl, budget_s=12.0, max_rows=4096):
     """Oracle (float64 numpy) on whole rows of the workload until ~budget_s of CPU work."""
     import oracle
     try:
@@ -73,7 +73,8 @@ def cpu_baseline(wl, budget_s=12.0, max_rows=64):
     vis = [r.visible for r in oracle.row_layout(wl.seq_lens_k, wl.cu_seqlens_q)]
     t0 = time.perf_counter()
     done = 0
-    for t in range(min(max_rows, wl.num_rows)):
+    order = [t % wl.num_rows for t in range(max_rows)]
+    for t in order:
         logits = oracle.indexer_logits(wl.q_idx, wl.w, wl.index_cache, wl.block_table, wl.seq_lens_k,
                                        wl.cu_seqlens_q, cfg.page_size, cfg.idx_kind, rows=[t])[t]
         idx = oracle.topk_row(logits, vis[t], cfg.topk)
@@ -86,8 +87,21 @@ def cpu_baseline(wl, budget_s=12.0, max_rows=64):
             break
     el = time.perf_counter() - t0
     return {"value": done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {done} of {wl.num_rows} decode rows of the same workload, all three stages "
-                      f"(float64 numpy), {el:.1f} s"}
+            "sample": f"{done} decode rows (rows 0.. of the {wl.num_rows}-row batch, cycling), all three "
+                      f"stages per row (float64 numpy), {el:.1f} s"}
+
+
+def copy_calibration(mib):
+    """A plain copy of a known size: 2 * mib MiB of algorithmic HBM traffic
+    (mib read + mib written), to scale the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n}))
 
 
 def main():
@@ -98,7 +112,13 @@ def main():
     ap.add_argument("--workload", default="decode_b64_ragged")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB mebibytes (counter calibration)")
     args = ap.parse_args()
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the DSA step is not "

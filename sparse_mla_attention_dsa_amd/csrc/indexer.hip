@@ -13,11 +13,13 @@
 // and the head sum are lane-local, followed by two cross-lane adds. sigma >= 0
 // commutes with relu, so it multiplies the head sum once per key.
 //
-// Work split: one work-group per (row, chunk of 1024 keys). The four waves take
-// interleaved groups of 16 keys (one page holds 64 / 16 = 4 groups at P = 64),
-// read the keys straight from HBM into MFMA operand registers, and write one
-// fp32 logit per key. The kernel is bound by HBM: 132 bytes of cache per key
-// against 16384 fp8 MACs.
+// Work split: one work-group per (row, chunk of 512 keys); the hardware
+// dispatcher balances the ragged rows. The row's q is staged once in LDS. Each
+// wave owns 128 consecutive keys (8 groups of 16; a 64-token page holds 4
+// groups), issues all of their loads straight from HBM into MFMA operand
+// registers before computing anything (16 KB in flight per wave), and writes
+// one fp32 logit per key. The kernel is bound by HBM: 132 bytes of cache per
+// key against 16384 fp8 MACs.
 #include "device_common.h"
 #include "dsa_internal.h"
 
@@ -25,15 +27,16 @@ namespace dsa {
 namespace {
 
 constexpr int kIdxWaves = 4;
-constexpr int kIdxChunk = 1024;
-constexpr int kIdxUnroll = 4;
+constexpr int kIdxGroupsPerWave = 8;                               // 16 keys each
+constexpr int kIdxChunk = 16 * kIdxGroupsPerWave * kIdxWaves;      // 512 keys per work-group
 
 __device__ __forceinline__ f32x4 mfma_fp8_16x16x128(const i32x8& a, const i32x8& b, const f32x4& c) {
   // format 0 = fp8 e4m3 for both operands; E8M0 scale 127 = 2^0 for both.
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-__global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerParams p) {
+__global__ __launch_bounds__(64 * kIdxWaves) void indexer_fp8_kernel(IndexerParams p) {
+  __shared__ i32x8 q_lds[kIdxHeads * kIdxDim / 32];   // the row's q, 8 KB
   const BatchView& bv = p.batch;
   const int t = blockIdx.x;
   int b, j, q_len;
@@ -46,20 +49,46 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerParams p) {
   if (k0 >= visible) return;
   const int k_end = min(k0 + kIdxChunk, visible);
 
+  const int tid = threadIdx.x;
   const int lane = lane_id();
-  const int wave = wave_id();
+  const int wave = __builtin_amdgcn_readfirstlane(wave_id());   // uniform: scalar page lookups
   const int g = lane >> 4;   // lane group: which 32-byte slice of the 128-wide dot product
   const int c = lane & 15;   // head (A rows) / key (B columns) inside a 16-wide tile
 
-  // q of this row as four 16-head A operands: lane (c, g) holds head 16m + c,
-  // bytes [32g, 32g + 32) of the 128-byte row.
-  const uint8_t* qrow = static_cast<const uint8_t*>(p.q) + (int64_t)t * (kIdxHeads * kIdxDim);
-  i32x8 qa[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-    qa[m] = *reinterpret_cast<const i32x8*>(qrow + (16 * m + c) * kIdxDim + 32 * g);
+  // q (64 x 128 fp8) is staged in LDS once for the four waves; its load is
+  // issued first and stored to LDS after the key loads are in flight
+  const i32x8* qrow = reinterpret_cast<const i32x8*>(static_cast<const uint8_t*>(p.q) +
+                                                     (int64_t)t * (kIdxHeads * kIdxDim));
+  const i32x8 qv = qrow[tid];
 
-  // Head weights in accumulator order: lane (c, g) holds rows 4g + i of each tile.
+  const int P = bv.page_size;
+  const int32_t* bt = bv.block_table + (int64_t)b * bv.max_pages_per_seq;
+  const int64_t scale_off = (int64_t)P * kIdxDim;
+  const int wbase = k0 + 16 * kIdxGroupsPerWave * wave;   // this wave's first key
+
+  // page of every group first (wave-uniform scalar loads, one wait), then every
+  // key load of this wave before any compute: lane (c, g) of group u holds key
+  // wbase + 16u + c, bytes [32g, 32g + 32)
+  int page[kIdxGroupsPerWave];
+#pragma unroll
+  for (int u = 0; u < kIdxGroupsPerWave; ++u) {
+    const int s0 = wbase + 16 * u;
+    page[u] = (s0 < k_end) ? bt[s0 / P] : -1;
+  }
+  i32x8 kb[kIdxGroupsPerWave];
+  float sig[kIdxGroupsPerWave];
+  bool ok[kIdxGroupsPerWave];
+#pragma unroll
+  for (int u = 0; u < kIdxGroupsPerWave; ++u) {
+    const int s0 = wbase + 16 * u;
+    ok[u] = page[u] >= 0 && page[u] < bv.num_pages;
+    const uint8_t* pg = p.cache + (int64_t)(ok[u] ? page[u] : 0) * p.page_bytes;
+    const int slot = (s0 % P) + c;   // < P: s0 is a multiple of 16 and P of 16
+    kb[u] = *reinterpret_cast<const i32x8*>(pg + (int64_t)slot * kIdxDim + 32 * g);
+    sig[u] = *reinterpret_cast<const float*>(pg + scale_off + 4 * slot);
+  }
+
+  // head weights in accumulator order: lane (c, g) holds rows 4g + i of each tile
   float wv[16];
   const float* wrow = p.w + (int64_t)t * kIdxHeads;
 #pragma unroll
@@ -69,46 +98,30 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerParams p) {
     for (int i = 0; i < 4; ++i) wv[4 * m + i] = w4[i];
   }
 
-  const int P = bv.page_size;
-  const int32_t* bt = bv.block_table + (int64_t)b * bv.max_pages_per_seq;
-  float* out = p.logits + (int64_t)t * p.stride;
-  const int64_t scale_off = (int64_t)P * kIdxDim;
+  q_lds[tid] = qv;
+  __syncthreads();
+  // q as four 16-head A operands: lane (c, g) holds head 16m + c, bytes [32g, 32g + 32)
+  i32x8 qa[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) qa[m] = q_lds[(16 * m + c) * (kIdxDim / 32) + g];
 
-  for (int base = k0 + 16 * wave; base < k_end; base += 16 * kIdxWaves * kIdxUnroll) {
-    i32x8 kb[kIdxUnroll];
-    float sig[kIdxUnroll];
-    bool ok[kIdxUnroll];
+  float* out = p.logits + (int64_t)t * p.stride;
 #pragma unroll
-    for (int u = 0; u < kIdxUnroll; ++u) {
-      const int s0 = base + u * 16 * kIdxWaves;
-      ok[u] = false;
-      sig[u] = 0.f;
-      if (s0 < k_end) {
-        const int page = bt[s0 / P];
-        ok[u] = page >= 0 && page < bv.num_pages;
-        const uint8_t* pg = p.cache + (int64_t)(ok[u] ? page : 0) * p.page_bytes;
-        const int slot = (s0 % P) + c;
-        kb[u] = *reinterpret_cast<const i32x8*>(pg + (int64_t)slot * kIdxDim + 32 * g);
-        sig[u] = *reinterpret_cast<const float*>(pg + scale_off + 4 * slot);
-      }
+  for (int u = 0; u < kIdxGroupsPerWave; ++u) {
+    const int s0 = wbase + 16 * u;
+    if (s0 >= k_end) break;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    float part = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const f32x4 acc = mfma_fp8_16x16x128(qa[m], kb[u], zero);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part = fmaf(wv[4 * m + i], fmaxf(acc[i], 0.f), part);
     }
-#pragma unroll
-    for (int u = 0; u < kIdxUnroll; ++u) {
-      const int s0 = base + u * 16 * kIdxWaves;
-      if (s0 >= k_end) break;
-      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-      float part = 0.f;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const f32x4 acc = mfma_fp8_16x16x128(qa[m], kb[u], zero);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) part = fmaf(wv[4 * m + i], fmaxf(acc[i], 0.f), part);
-      }
-      part += shfl_xor_f(part, 16);
-      part += shfl_xor_f(part, 32);
-      const int s = s0 + c;
-      if (g == 0 && s < k_end) out[s] = ok[u] ? part * sig[u] : -INFINITY;
-    }
+    part += shfl_xor_f(part, 16);
+    part += shfl_xor_f(part, 32);
+    const int s = s0 + c;
+    if (g == 0 && s < k_end) out[s] = ok[u] ? part * sig[u] : -INFINITY;
   }
 }
 

@@ -4,63 +4,98 @@
 // forward_indexer takes topk(min(topk, seq_len)) and pads with -1;
 // _forward_cuda_k_only relies on rows of length <= k giving [0 .. len-1, -1 ...].)
 //
-// One work-group of 1024 threads per row. Scores become order-preserving 32-bit
+// One work-group of 512 threads per row. Scores become order-preserving 32-bit
 // keys. A radix select on the key bits (12 + 12 + 8 bits, three LDS histograms)
 // finds the exact k-th largest key `thr` and how many of the k winners are equal
 // to it. A last ordered pass writes the winners in ascending position order:
 // everything above `thr`, plus the first `need` positions equal to `thr`, so ties
-// go to the lower positions. Rows of up to 32768 scores are kept in LDS after the
-// first read from HBM; longer rows are re-read from global memory (L2) by each
-// pass.
+// go to the lower positions.
+//
+// Rows of up to 32768 scores are read from HBM once: each thread keeps sixteen
+// 16-byte loads in flight (the whole row is requested at once), converts them to
+// keys into LDS and counts the first digit on the way. Longer rows are re-read
+// from global memory (L2) by each pass. Every pass handles 8 consecutive
+// positions per thread; the ordered output pass needs one block-wide scan per
+// 4096 positions.
 #include "device_common.h"
 #include "dsa_internal.h"
 
 namespace dsa {
 namespace {
 
-constexpr int kTkThreads = 1024;
+constexpr int kTkThreads = 512;
 constexpr int kTkWaves = kTkThreads / kWave;
 constexpr int kTkCache = 32768;
 constexpr int kTkBins = 4096;
+constexpr int kTkLoadUnroll = 16;          // float4 loads in flight per thread
+constexpr int kTkPer = 8;                  // consecutive positions per thread per pass step
 
 struct TopkShared {
   uint32_t hist[kTkBins];
-  uint32_t keys[kTkCache];
-  uint32_t wave_sum[kTkWaves];
-  uint32_t wave_cnt[2][2][kTkWaves];
+  alignas(16) uint32_t keys[kTkCache];
+  uint32_t wave_sum[2][kTkWaves];
   uint32_t sel_bin;
   uint32_t sel_above;
 };
 
-__device__ __forceinline__ uint32_t load_key(const float* __restrict__ row, const TopkShared& sh,
-                                             bool cached, int i) {
-  return cached ? sh.keys[i] : ordered_key(row[i]);
+// Keys of positions [i, i + 8) (i a multiple of 8); positions >= n give 0.
+__device__ __forceinline__ void load8(const float* __restrict__ row, const TopkShared& sh, bool cached,
+                                      int n, int i, uint32_t (&u)[kTkPer]) {
+  if (cached) {
+    const i32x4 a = *reinterpret_cast<const i32x4*>(sh.keys + i);
+    const i32x4 b = *reinterpret_cast<const i32x4*>(sh.keys + i + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { u[e] = (uint32_t)a[e]; u[4 + e] = (uint32_t)b[e]; }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kTkPer; ++e) {
+      const int q = i + e < n ? i + e : n - 1;   // clamped: always in bounds
+      u[e] = ordered_key(row[q]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < kTkPer; ++e) u[e] = (i + e < n) ? u[e] : 0u;
 }
 
-// Find the largest bin b (of nbins, counted in `hist`) whose suffix count
-// sum_{b' >= b} hist[b'] reaches `need`; return b and the count strictly above it.
-__device__ void select_bin(TopkShared& sh, int nbins, uint32_t need, uint32_t* bin, uint32_t* above) {
-  const int tid = threadIdx.x;
-  const int per = nbins / kTkThreads > 0 ? nbins / kTkThreads : 1;
-  const int active = nbins / per;       // threads that own bins
-  // thread tid owns bins [nbins - per*(tid+1), nbins - per*tid), counted from the top
-  uint32_t local = 0;
-  if (tid < active) {
-    for (int q = 0; q < per; ++q) local += sh.hist[nbins - 1 - per * tid - q];
-  }
-  // block-wide exclusive scan of `local` in thread order
+// Inclusive scan of v over the work-group in thread order; returns the
+// inclusive prefix and stores the total in *total. One barrier; `buf` selects
+// the double-buffered wave totals so consecutive calls need no extra barrier.
+__device__ __forceinline__ uint32_t block_scan(TopkShared& sh, uint32_t v, int buf, uint32_t* total) {
   const int lane = lane_id(), wave = wave_id();
-  uint32_t incl = local;
+  uint32_t incl = v;
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {
-    const uint32_t v = __shfl_up(incl, d, kWave);
-    if (lane >= d) incl += v;
+    const uint32_t o = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += o;
   }
-  if (lane == kWave - 1) sh.wave_sum[wave] = incl;
+  if (lane == kWave - 1) sh.wave_sum[buf][wave] = incl;
   __syncthreads();
-  uint32_t before = incl - local;
-  for (int w = 0; w < wave; ++w) before += sh.wave_sum[w];
-  if (tid < active && before < need && before + local >= need) {
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kTkWaves; ++w) {
+    const uint32_t s = sh.wave_sum[buf][w];
+    before += (w < wave) ? s : 0u;
+    tot += s;
+  }
+  *total = tot;
+  return before + incl;
+}
+
+// Largest bin b whose suffix count sum_{b' >= b} hist[b'] reaches `need`; also
+// the count strictly above it.
+__device__ void select_bin(TopkShared& sh, int nbins, uint32_t need, int buf, uint32_t* bin,
+                           uint32_t* above) {
+  const int tid = threadIdx.x;
+  const int per = nbins >= kTkThreads ? nbins / kTkThreads : 1;
+  const int active = nbins / per;
+  // thread tid owns bins nbins-1-per*tid down to nbins-per*(tid+1), counted from the top
+  uint32_t local = 0;
+  if (tid < active)
+    for (int q = 0; q < per; ++q) local += sh.hist[nbins - 1 - per * tid - q];
+  uint32_t total;
+  const uint32_t incl = block_scan(sh, local, buf, &total);
+  const uint32_t before = incl - local;
+  if (tid < active && before < need && incl >= need) {
     uint32_t cum = before;
     for (int q = 0; q < per; ++q) {
       const int bb = nbins - 1 - per * tid - q;
@@ -99,80 +134,122 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
 
   const float* row = p.logits + (int64_t)t * p.stride;
   const bool cached = n <= kTkCache;
-
-  // level 0: bits 31..20, loading the row (and caching its keys)
   for (int i = tid; i < kTkBins; i += kTkThreads) sh.hist[i] = 0;
   __syncthreads();
-  for (int i = tid; i < n; i += kTkThreads) {
-    const uint32_t u = ordered_key(row[i]);
-    if (cached) sh.keys[i] = u;
-    atomicAdd(&sh.hist[u >> 20], 1u);
+
+  // ---- level 0 (bits 31..20) while reading the row once ----
+  const bool vec = ((reinterpret_cast<uintptr_t>(row) & 15u) == 0);
+  const int n4 = vec ? n / 4 : 0;
+  for (int base = 0; base < n4; base += kTkThreads * kTkLoadUnroll) {
+    f32x4 v[kTkLoadUnroll];
+#pragma unroll
+    for (int u = 0; u < kTkLoadUnroll; ++u) {
+      int i4 = base + u * kTkThreads + tid;
+      i4 = i4 < n4 ? i4 : n4 - 1;               // clamped: always in bounds
+      v[u] = reinterpret_cast<const f32x4*>(row)[i4];
+    }
+#pragma unroll
+    for (int u = 0; u < kTkLoadUnroll; ++u) {
+      const int i4 = base + u * kTkThreads + tid;
+      if (i4 < n4) {
+        uint32_t kk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kk[e] = ordered_key(v[u][e]);
+          atomicAdd(&sh.hist[kk[e] >> 20], 1u);
+        }
+        if (cached)
+          *reinterpret_cast<i32x4*>(sh.keys + 4 * i4) = i32x4{(int)kk[0], (int)kk[1], (int)kk[2], (int)kk[3]};
+      }
+    }
+  }
+  for (int i = 4 * n4 + tid; i < n; i += kTkThreads) {
+    const uint32_t kk = ordered_key(row[i]);
+    if (cached) sh.keys[i] = kk;
+    atomicAdd(&sh.hist[kk >> 20], 1u);
   }
   __syncthreads();
   uint32_t need = (uint32_t)k;
   uint32_t bin, above;
-  select_bin(sh, kTkBins, need, &bin, &above);
+  select_bin(sh, kTkBins, need, 0, &bin, &above);
   uint32_t prefix = bin;
   need -= above;
 
-  // level 1: bits 19..8 among keys whose top 12 bits equal the prefix
+  // ---- level 1 (bits 19..8) among keys whose top 12 bits equal the prefix ----
   for (int i = tid; i < kTkBins; i += kTkThreads) sh.hist[i] = 0;
   __syncthreads();
-  for (int i = tid; i < n; i += kTkThreads) {
-    const uint32_t u = load_key(row, sh, cached, i);
-    if ((u >> 20) == prefix) atomicAdd(&sh.hist[(u >> 8) & 0xfffu], 1u);
+  for (int i = kTkPer * tid; i < n; i += kTkPer * kTkThreads) {
+    uint32_t u[kTkPer];
+    load8(row, sh, cached, n, i, u);
+#pragma unroll
+    for (int e = 0; e < kTkPer; ++e)
+      if (i + e < n && (u[e] >> 20) == prefix) atomicAdd(&sh.hist[(u[e] >> 8) & 0xfffu], 1u);
   }
   __syncthreads();
-  select_bin(sh, kTkBins, need, &bin, &above);
+  select_bin(sh, kTkBins, need, 1, &bin, &above);
   prefix = (prefix << 12) | bin;
   need -= above;
 
-  // level 2: bits 7..0 among keys whose top 24 bits equal the prefix
+  // ---- level 2 (bits 7..0) among keys whose top 24 bits equal the prefix ----
   for (int i = tid; i < 256; i += kTkThreads) sh.hist[i] = 0;
   __syncthreads();
-  for (int i = tid; i < n; i += kTkThreads) {
-    const uint32_t u = load_key(row, sh, cached, i);
-    if ((u >> 8) == prefix) atomicAdd(&sh.hist[u & 0xffu], 1u);
+  for (int i = kTkPer * tid; i < n; i += kTkPer * kTkThreads) {
+    uint32_t u[kTkPer];
+    load8(row, sh, cached, n, i, u);
+#pragma unroll
+    for (int e = 0; e < kTkPer; ++e)
+      if (i + e < n && (u[e] >> 8) == prefix) atomicAdd(&sh.hist[u[e] & 0xffu], 1u);
   }
   __syncthreads();
-  select_bin(sh, 256, need, &bin, &above);
+  select_bin(sh, 256, need, 0, &bin, &above);
   const uint32_t thr = (prefix << 8) | bin;
   need -= above;  // how many keys equal to thr are among the winners (>= 1)
 
-  // ordered output pass: position of a winner = winners before it
-  //   = (#keys > thr before it) + min(#keys == thr before it, need)
-  const int lane = lane_id(), wave = wave_id();
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // ---- ordered output ----
+  // position of a winner = (#keys > thr before it) + min(#keys == thr before it, need)
   uint32_t base_gt = 0, base_eq = 0;
-  int it = 0;
-  for (int i0 = 0; i0 < n; i0 += kTkThreads, ++it) {
-    const int i = i0 + tid;
-    const uint32_t u = i < n ? load_key(row, sh, cached, i) : 0u;
-    const bool gt = i < n && u > thr;
-    const bool eq = i < n && u == thr;
-    const uint64_t mgt = __ballot(gt);
-    const uint64_t meq = __ballot(eq);
-    const int buf = it & 1;
-    if (lane == 0) {
-      sh.wave_cnt[buf][0][wave] = (uint32_t)__popcll(mgt);
-      sh.wave_cnt[buf][1][wave] = (uint32_t)__popcll(meq);
+  int it = 1;
+  for (int i0 = 0; i0 < n; i0 += kTkPer * kTkThreads, ++it) {
+    const int i = i0 + kTkPer * tid;
+    uint32_t u[kTkPer];
+    if (i < n) {
+      load8(row, sh, cached, n, i, u);
+    } else {
+#pragma unroll
+      for (int e = 0; e < kTkPer; ++e) u[e] = 0u;
     }
-    __syncthreads();
-    uint32_t off_gt = 0, off_eq = 0, tot_gt = 0, tot_eq = 0;
-    for (int w = 0; w < kTkWaves; ++w) {
-      const uint32_t a = sh.wave_cnt[buf][0][w], e = sh.wave_cnt[buf][1][w];
-      if (w < wave) { off_gt += a; off_eq += e; }
-      tot_gt += a;
-      tot_eq += e;
+    uint32_t cgt = 0, ceq = 0;
+#pragma unroll
+    for (int e = 0; e < kTkPer; ++e) {
+      const bool valid = i + e < n;
+      cgt += (valid && u[e] > thr) ? 1u : 0u;
+      ceq += (valid && u[e] == thr) ? 1u : 0u;
     }
-    const uint32_t gt_before = base_gt + off_gt + (uint32_t)__popcll(mgt & lt_mask);
-    const uint32_t eq_before = base_eq + off_eq + (uint32_t)__popcll(meq & lt_mask);
-    if (gt || (eq && eq_before < need)) {
-      const uint32_t pos = gt_before + (eq_before < need ? eq_before : need);
-      if (pos < (uint32_t)k) out[pos] = i;
+    // counts per thread are <= 8 and per block <= 4096: pack (gt, eq) in one word
+    uint32_t total;
+    const uint32_t packed = (cgt << 16) | ceq;
+    const uint32_t excl = block_scan(sh, packed, it & 1, &total) - packed;
+    uint32_t gt_before = base_gt + (excl >> 16);
+    uint32_t eq_before = base_eq + (excl & 0xffffu);
+    if (packed) {
+#pragma unroll
+      for (int e = 0; e < kTkPer; ++e) {
+        const bool valid = i + e < n;
+        if (valid && u[e] > thr) {
+          const uint32_t pos = gt_before + (eq_before < need ? eq_before : need);
+          if (pos < (uint32_t)k) out[pos] = i + e;
+          ++gt_before;
+        } else if (valid && u[e] == thr) {
+          if (eq_before < need) {
+            const uint32_t pos = gt_before + eq_before;
+            if (pos < (uint32_t)k) out[pos] = i + e;
+          }
+          ++eq_before;
+        }
+      }
     }
-    base_gt += tot_gt;
-    base_eq += tot_eq;
+    base_gt += total >> 16;
+    base_eq += total & 0xffffu;
     if (base_gt + (base_eq < need ? base_eq : need) >= (uint32_t)k) break;
   }
 }
