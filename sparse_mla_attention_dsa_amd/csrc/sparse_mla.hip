@@ -10,23 +10,28 @@
 //   z_i = scale * (q[t,h] . C_i),  out[t,h] = sum_i softmax(z)_i C_i[:512],
 //   lse[t,h] = log sum_i exp(z_i).
 //
-// bf16 path (Dl = 512, Dr = 64, Hm a multiple of 64). One work-group of four
+// bf16 path (Dl = 512, Dr = 64, Hm a multiple of 64). One work-group of eight
 // waves handles one (row, split of the top-k list, group of 64 heads):
 //   * the split's positions are resolved once through the block table into
 //     cache-row ids in LDS, skipping -1 / out-of-range entries (so the -1 tail
 //     of short rows costs nothing);
-//   * gathered rows arrive 32 at a time: global -> VGPR (issued one tile ahead)
-//     -> LDS, with the row stride padded to 1168 bytes so that both LDS access
-//     patterns below are free of bank conflicts;
-//   * scores: wave w computes S^T[32 rows x 16 heads] = C_tile . Q_w^T with
+//   * gathered rows arrive 32 at a time straight from HBM into a ring of three
+//     LDS tiles (global_load_lds, 16 bytes per lane): two tiles are in flight
+//     while the third is computed on. Rows are stored dense with an XOR swizzle
+//     of their 16-byte chunks so that both LDS read patterns below are free of
+//     bank conflicts;
+//   * scores: waves w and w + 4 compute S^T[32 rows x 16 heads] = C_tile . Q^T
+//     over the two halves of the 576-wide contraction with
 //     v_mfma_f32_16x16x32_bf16 (rows = M from LDS, heads = N from registers:
-//     each wave keeps its 16 heads x 576 of q in VGPRs);
+//     each wave keeps its 16 heads x 288 of q in VGPRs) and exchange the
+//     halves through LDS;
 //   * online softmax in fp32, base 2, with lazy rescaling: the running maximum
 //     of a head only moves when a tile exceeds it by more than 2^8, so the
 //     accumulator rescale is skipped on most tiles;
 //   * probabilities (bf16) and the per-head rescale factors go through LDS so
-//     that wave w can compute O[64 heads x 128 value columns] += P . V_tile,
-//     again on 16x16x32 bf16 MFMA (heads = M, value columns = N);
+//     that wave w can compute O[64 heads x 64 value columns] += P . V_tile,
+//     again on 16x16x32 bf16 MFMA (heads = M, value columns = N). The small
+//     per-wave register footprint (q 36, O 64) gives two waves per SIMD;
 //   * single split: out = O / l in bf16 and lse; several splits: fp32 partials
 //     (O / l, lse) merged by mla_combine_kernel.
 // Work-groups are ordered so that the head groups of one (row, split) unit, and
@@ -38,36 +43,81 @@
 namespace dsa {
 namespace {
 
-constexpr int kMlaThreads = 256;
-constexpr int kRowBytes = kMlaDqk * 2;                  // 1152
-constexpr int kLdsRowStride = kRowBytes + 16;           // 1168
-constexpr int kChunksPerRow = kRowBytes / 16;           // 72
-constexpr int kTileChunks = kMlaTile * kChunksPerRow;   // 2304
-constexpr int kChunksPerThread = kTileChunks / kMlaThreads;  // 9
+constexpr int kMlaThreads = 512;
+constexpr int kMlaWaves = kMlaThreads / kWave;          // 8
+constexpr int kRowBytes = kMlaDqk * 2;                  // 1152: one cached latent row
+constexpr int kChunksPerRow = kRowBytes / 16;           // 72 chunks of 16 bytes
+constexpr int kTileBytes = kMlaTile * kRowBytes;        // 36864
+constexpr int kDmaPerTile = kTileBytes / 1024;          // 36 wave-wide 1 KB copies
+constexpr int kRing = 3;                                // tiles resident: 1 computing, 2 landing
+constexpr int kEntriesPerThread = kMlaMaxEntriesPerBlock / kMlaThreads;  // 4
+constexpr int kKSteps = kMlaDqk / 2 / 32;               // 9 K-steps of 32 in each half of 576
+constexpr int kPRow = kMlaTile + 4;                     // P row stride (72 B): conflict-free rows
 constexpr float kRescaleThreshold = 8.0f;               // log2 units
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-
-static_assert(kTileChunks % kMlaThreads == 0, "tile must split evenly over the threads");
 
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 
 struct MlaShared {
+  // Gathered rows, dense (1152 B per row). Inside row r the 16-byte chunk c is
+  // stored at chunk position c ^ swz(r) (see swz).
+  alignas(16) uint8_t kv[kRing][kTileBytes];
   int32_t rowid[kMlaMaxEntriesPerBlock];
-  alignas(16) uint8_t kv[kMlaTile * kLdsRowStride];
-  alignas(16) uint16_t pbuf[kMlaHeadsPerGroup * kMlaTile];  // [head][row] bf16 bits
+  alignas(16) uint16_t pbuf[kMlaHeadsPerGroup * kPRow];     // [head][row] bf16 bits, padded rows
+  alignas(16) f32x4 sx[kMlaWaves / 2][2][kWave];            // second-half partial scores
   alignas(16) float alpha[kMlaHeadsPerGroup];
   alignas(16) float lsum[kMlaHeadsPerGroup];
   int flag[2];
-  int wave_cnt[2][kMlaThreads / kWave];
+  int wave_sum[kMlaWaves];
 };
+
+// Chunk swizzle of row r (bits 0-2 of r, bit 3 of r folded onto bits 0-1):
+// sixteen consecutive rows reading the same logical chunk, and the rows
+// {j, j+4, j+8, j+12} reading the same value column, hit distinct banks for
+// both 8-lane (128 B) and 16-lane (256 B) LDS service groups. Rows r and r + 16
+// share the swizzle.
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ (((row >> 3) & 1) * 3); }
+
+// max of v over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups), with the
+// gfx950 lane swaps (VALU, no LDS round trip)
+__device__ __forceinline__ float max_over_groups(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float sum_over_groups(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(kMlaThreads, 1) void mla_bf16_kernel(MlaParams p) {
+// Copy 16 bytes per lane from global memory straight into LDS: lane l's bytes
+// land at LDS offset lds_off + 16 * l (wave-uniform lds_off). M0 is set here
+// explicitly; completion is tracked with vmcnt by the caller.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(gsrc), "s"(lds_off) : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>(p);   // LDS aperture: low 32 bits are the offset
+}
+
+__global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
   __shared__ MlaShared sh;
   const BatchView& bv = p.batch;
   const int T = bv.num_rows;
@@ -88,8 +138,11 @@ __global__ __launch_bounds__(kMlaThreads, 1) void mla_bf16_kernel(MlaParams p) {
   const int s = unit % S;
 
   const int tid = threadIdx.x;
-  const int lane = lane_id(), wave = wave_id();
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(wave_id());
   const int g = lane >> 4, c = lane & 15;
+  const int ht = wave & 3;     // score role: heads 16*ht .. 16*ht+15 of the group
+  const int kh = wave >> 2;    //             half of the 576-wide contraction
 
   int b, jrow, q_len;
   row_to_seq(t, bv.cu_seqlens_q, bv.num_seqs, &b, &jrow, &q_len);
@@ -99,195 +152,241 @@ __global__ __launch_bounds__(kMlaThreads, 1) void mla_bf16_kernel(MlaParams p) {
   if (seq_len > addressable) seq_len = addressable;
   const int32_t* bt = bv.block_table + (int64_t)b * bv.max_pages_per_seq;
 
-  // ---- resolve this split's entries into cache-row ids (compacted) ----
+  const int head0 = hg * kMlaHeadsPerGroup;
+  const int Hm = p.heads;
+  // ---- q (loads overlap the index resolution below): this wave's 16 heads, its half of the contraction (N operand) ----
+  const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
+                         ((int64_t)t * Hm + head0 + 16 * ht + c) * kMlaDqk + kh * (kMlaDqk / 2);
+  bf16x8 qf[kKSteps];
+#pragma unroll
+  for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks + 8 * g);
+
+  // ---- resolve this split's entries into cache-row ids (compacted, in order) ----
   const int e_begin = s * p.entries_per_split;
   int e_cnt = p.k - e_begin;
   if (e_cnt > p.entries_per_split) e_cnt = p.entries_per_split;
   if (e_cnt < 0) e_cnt = 0;
   const int32_t* idx = p.topk_idx + (int64_t)t * p.k + e_begin;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int nvalid = 0;
-  for (int e0 = 0, it = 0; e0 < e_cnt; e0 += kMlaThreads, ++it) {
-    const int e = e0 + tid;
-    bool valid = false;
-    int32_t rid = 0;
-    if (e < e_cnt) {
-      const int pos = idx[e];
-      if (pos >= 0 && pos < seq_len) {
-        const int page = bt[pos / P];
-        if (page >= 0 && page < bv.num_pages) {
-          valid = true;
-          rid = page * P + pos % P;
-        }
-      }
-    }
-    const uint64_t m = __ballot(valid);
-    const int buf = it & 1;
-    if (lane == 0) sh.wave_cnt[buf][wave] = __popcll(m);
-    __syncthreads();
-    int off = 0, tot = 0;
+  int pos[kEntriesPerThread], page[kEntriesPerThread];
 #pragma unroll
-    for (int w = 0; w < kMlaThreads / kWave; ++w) {
-      const int v = sh.wave_cnt[buf][w];
-      off += (w < wave) ? v : 0;
-      tot += v;
-    }
-    if (valid) sh.rowid[nvalid + off + __popcll(m & lt_mask)] = rid;
-    nvalid += tot;
+  for (int q = 0; q < kEntriesPerThread; ++q) {       // all index loads in flight
+    const int e = kEntriesPerThread * tid + q;
+    pos[q] = (e < e_cnt) ? idx[e] : -1;
   }
+#pragma unroll
+  for (int q = 0; q < kEntriesPerThread; ++q) {       // then all page lookups
+    const bool in = pos[q] >= 0 && pos[q] < seq_len;
+    page[q] = in ? bt[pos[q] / P] : -1;
+  }
+  int nmine = 0;
+#pragma unroll
+  for (int q = 0; q < kEntriesPerThread; ++q) nmine += (page[q] >= 0 && page[q] < bv.num_pages) ? 1 : 0;
+  int incl = nmine;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int o = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += o;
+  }
+  if (lane == kWave - 1) sh.wave_sum[wave] = incl;
   if (tid < 2) sh.flag[tid] = 0;
   __syncthreads();
+  int nvalid = 0, w_off = 0;
+#pragma unroll
+  for (int w = 0; w < kMlaWaves; ++w) {
+    const int v = sh.wave_sum[w];
+    w_off += (w < wave) ? v : 0;
+    nvalid += v;
+  }
+  {
+    int o = w_off + incl - nmine;
+#pragma unroll
+    for (int q = 0; q < kEntriesPerThread; ++q)
+      if (page[q] >= 0 && page[q] < bv.num_pages) sh.rowid[o++] = page[q] * P + pos[q] % P;
+  }
+  __syncthreads();
 
-  const int head0 = hg * kMlaHeadsPerGroup;          // first head of the group
-  const int Hm = p.heads;
   const float scale_log2 = p.softmax_scale * kLog2e;
-
-  // ---- q of this wave's 16 heads (N operand of the score MFMA) ----
-  const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
-                         ((int64_t)t * Hm + head0 + 16 * wave + c) * kMlaDqk;
-  bf16x8 qf[kMlaDqk / 32];
-#pragma unroll
-  for (int ks = 0; ks < kMlaDqk / 32; ++ks)
-    qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks + 8 * g);
-
-  f32x4 acc_o[4][8];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) acc_o[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY;   // running max (log2 units) of head 16*wave + c
-  float l_part = 0.f;        // this lane's share of the softmax denominator
-
   const uint8_t* kvbase = static_cast<const uint8_t*>(p.kv);
   const int n_tiles = (nvalid + kMlaTile - 1) / kMlaTile;
 
-  i32x4 stage[kChunksPerThread];
-  auto load_tile = [&](int tile) {
+  // one tile = 36 wave-wide 1 KB copies; wave w issues copies w, w+8, ... (waves
+  // 0-3 issue five, waves 4-7 four). Copy i fills LDS chunks 64i .. 64i+63.
+  auto issue_tile = [&](int tile) {
+    uint8_t* dst = sh.kv[tile % kRing];
+    const uint8_t* src[5];
 #pragma unroll
-    for (int i = 0; i < kChunksPerThread; ++i) {
-      const int cid = tid + kMlaThreads * i;
-      const int r = cid / kChunksPerRow, col = cid % kChunksPerRow;
+    for (int q = 0; q < 5; ++q) {                       // row ids first (LDS reads) ...
+      const int i = wave + kMlaWaves * q;
+      const int chunk = 64 * i + lane;
+      const int r = chunk / kChunksPerRow;
+      const int posc = chunk % kChunksPerRow;
+      const int col = posc ^ swz(r);                    // logical chunk stored at posc
       const int e = tile * kMlaTile + r;
-      if (e < nvalid) {
-        const int64_t rid = sh.rowid[e];
-        stage[i] = *reinterpret_cast<const i32x4*>(kvbase + rid * kRowBytes + col * 16);
-      } else {
-        stage[i] = i32x4{0, 0, 0, 0};
-      }
+      // rows past the end re-read the split's first row; their scores are masked
+      const int64_t rid = (i < kDmaPerTile) ? sh.rowid[e < nvalid ? e : 0] : 0;
+      src[q] = kvbase + rid * kRowBytes + col * 16;
     }
-  };
-  auto store_tile = [&]() {
 #pragma unroll
-    for (int i = 0; i < kChunksPerThread; ++i) {
-      const int cid = tid + kMlaThreads * i;
-      const int r = cid / kChunksPerRow, col = cid % kChunksPerRow;
-      *reinterpret_cast<i32x4*>(sh.kv + r * kLdsRowStride + col * 16) = stage[i];
+    for (int q = 0; q < 5; ++q) {                       // ... then all copies back to back
+      const int i = wave + kMlaWaves * q;
+      if (i < kDmaPerTile) lds_dma16(src[q], lds_offset(dst + 1024 * i));
     }
   };
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile();
+  // Consume q here: the compiler then knows its loads have completed, and it
+  // places no vector-memory waits inside the tile loop, where they would also
+  // drain the (to it invisible) tile copies in flight.
+#pragma unroll
+  for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" :: "v"(qf[ks]));
+
+  if (n_tiles > 0) issue_tile(0);
+  if (n_tiles > 1) issue_tile(1);
+
+  f32x4 acc_o[4][4];   // O[heads 16mt + 4g + i][value column 64*wave + 16nt + c]
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc_o[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY;   // running max (log2 units) of head 16*ht + c
+  float l_part = 0.f;        // this lane's share of the softmax denominator
+
+  // score operand: rows c and 16 + c share a swizzle; this wave's half of the row
+  const int sw_c = swz(c);
+  const int a_row = c * kRowBytes;
+  const int kchunk0 = kh * (kMlaDqk / 2 / 8);        // first 16-byte chunk of the half (36)
+  // value reads: slot jj < 4 -> row 4g + jj, slot jj >= 4 -> row 16 + 4g + jj - 4
+  int v_row[8], v_sw[8];
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    const int r = (jj < 4) ? 4 * g + jj : 16 + 4 * g + (jj - 4);
+    v_row[jj] = r * kRowBytes + 2 * (c & 7);
+    v_sw[jj] = swz(r);
+  }
+
+  // tile 0 visible before the loop
+  if (n_tiles > 1) {
+    if (wave < 4) wait_vmcnt<5>(); else wait_vmcnt<4>();
+  } else {
+    wait_vmcnt<0>();
   }
   __syncthreads();
 
+  // Per tile: scores -> [barrier B] -> copies of tile + 2, softmax, wait for
+  // tile + 1 -> [barrier C] -> P.V. Barrier B also guarantees that every wave
+  // has finished P.V of the previous tile, so its ring slot can be refilled.
   for (int tile = 0; tile < n_tiles; ++tile) {
-    if (tile + 1 < n_tiles) load_tile(tile + 1);   // in flight during this tile
+    const uint8_t* kvt = sh.kv[tile % kRing];
 
-    // ---- scores for 32 rows x this wave's 16 heads ----
-    f32x4 sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
-    const uint8_t* r0 = sh.kv + c * kLdsRowStride + 16 * g;
-    const uint8_t* r1 = r0 + 16 * kLdsRowStride;
+    // ---- partial scores: 32 rows x 16 heads over this wave's half ----
+    f32x4 sa0 = {0.f, 0.f, 0.f, 0.f}, sa1 = sa0, sb0 = sa0, sb1 = sa0;
 #pragma unroll
-    for (int ks = 0; ks < kMlaDqk / 32; ++ks) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(r0 + 64 * ks);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(r1 + 64 * ks);
-      sc0 = mfma_bf16(a0, qf[ks], sc0);
-      sc1 = mfma_bf16(a1, qf[ks], sc1);
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      const int o = ((kchunk0 + 4 * ks + g) ^ sw_c) << 4;
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kvt + a_row + o);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kvt + a_row + 16 * kRowBytes + o);
+      if (ks & 1) {
+        sb0 = mfma_bf16(a0, qf[ks], sb0);
+        sb1 = mfma_bf16(a1, qf[ks], sb1);
+      } else {
+        sa0 = mfma_bf16(a0, qf[ks], sa0);
+        sa1 = mfma_bf16(a1, qf[ks], sa1);
+      }
     }
-    // lane (c, g) holds head c, rows 4g+i (sc0) and 16+4g+i (sc1)
-    const int rowbase = tile * kMlaTile;
-    float sv[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sv[i] = (rowbase + 4 * g + i < nvalid) ? sc0[i] * scale_log2 : -INFINITY;
-      sv[4 + i] = (rowbase + 16 + 4 * g + i < nvalid) ? sc1[i] * scale_log2 : -INFINITY;
+    const f32x4 own0 = sa0 + sb0, own1 = sa1 + sb1;
+    if (kh == 1) {
+      sh.sx[ht][0][lane] = own0;
+      sh.sx[ht][1][lane] = own1;
     }
-    float mx = sv[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    float alpha = 1.f;
-    if (mx > m_ref + kRescaleThreshold) {
-      alpha = exp2f(m_ref - mx);
-      m_ref = mx;
-      l_part *= alpha;
-    }
-    if (__ballot(alpha != 1.f) != 0ull && lane == 0) sh.flag[tile & 1] = 1;
-    uint16_t pb[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float pr = exp2f(sv[i] - m_ref);
-      l_part += pr;
-      pb[i] = f32_to_bf16_bits(pr);
-    }
-    uint16_t* prow = sh.pbuf + (16 * wave + c) * kMlaTile;
-    *reinterpret_cast<u16x4*>(prow + 4 * g) = u16x4{pb[0], pb[1], pb[2], pb[3]};
-    *reinterpret_cast<u16x4*>(prow + 16 + 4 * g) = u16x4{pb[4], pb[5], pb[6], pb[7]};
-    if (g == 0) sh.alpha[16 * wave + c] = alpha;
-    __syncthreads();
+    __syncthreads();                                     // barrier B
+    if (tile + 2 < n_tiles) issue_tile(tile + 2);       // slot of tile - 1: free after B
 
-    // ---- O[64 heads x value columns 128w..128w+127] += P . V ----
+    if (kh == 0) {
+      const f32x4 sc0 = own0 + sh.sx[ht][0][lane];
+      const f32x4 sc1 = own1 + sh.sx[ht][1][lane];
+      // lane (c, g) holds head c, rows 4g+i (sc0) and 16+4g+i (sc1)
+      const int rowbase = tile * kMlaTile;
+      float sv[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[i] = (rowbase + 4 * g + i < nvalid) ? sc0[i] * scale_log2 : -INFINITY;
+        sv[4 + i] = (rowbase + 16 + 4 * g + i < nvalid) ? sc1[i] * scale_log2 : -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                       fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+      mx = max_over_groups(mx);
+      float alpha = 1.f;
+      if (mx > m_ref + kRescaleThreshold) {
+        alpha = __builtin_amdgcn_exp2f(m_ref - mx);
+        m_ref = mx;
+        l_part *= alpha;
+      }
+      if (__ballot(alpha != 1.f) != 0ull && lane == 0) sh.flag[tile & 1] = 1;
+      uint16_t pb[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float pr = __builtin_amdgcn_exp2f(sv[i] - m_ref);
+        l_part += pr;
+        pb[i] = f32_to_bf16_bits(pr);
+      }
+      uint16_t* prow = sh.pbuf + (16 * ht + c) * kPRow;
+      *reinterpret_cast<u16x4*>(prow + 4 * g) = u16x4{pb[0], pb[1], pb[2], pb[3]};
+      *reinterpret_cast<u16x4*>(prow + 16 + 4 * g) = u16x4{pb[4], pb[5], pb[6], pb[7]};
+      if (g == 0) sh.alpha[16 * ht + c] = alpha;
+    }
+    // tile + 1 has landed once at most tile + 2's copies are pending
+    if (tile + 1 < n_tiles) {
+      if (tile + 2 < n_tiles) {
+        if (wave < 4) wait_vmcnt<5>(); else wait_vmcnt<4>();
+      } else {
+        wait_vmcnt<0>();
+      }
+    }
+    __syncthreads();                                     // barrier C
+
+    // ---- O[64 heads x value columns 64w..64w+63] += P . V ----
     if (sh.flag[tile & 1]) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const f32x4 a4 = *reinterpret_cast<const f32x4*>(sh.alpha + 16 * mt + 4 * g);
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) acc_o[mt][nt] *= a4;
+        for (int nt = 0; nt < 4; ++nt) acc_o[mt][nt] *= a4;
       }
     }
     if (tid == 0) sh.flag[(tile + 1) & 1] = 0;
     bf16x8 pa[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const uint16_t* pr = sh.pbuf + (16 * mt + c) * kMlaTile;
+      const uint16_t* pr = sh.pbuf + (16 * mt + c) * kPRow;
       const u16x4 lo = *reinterpret_cast<const u16x4*>(pr + 4 * g);
       const u16x4 hi = *reinterpret_cast<const u16x4*>(pr + 16 + 4 * g);
       const u16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       pa[mt] = __builtin_bit_cast(bf16x8, v);
     }
-    const uint16_t* kv16 = reinterpret_cast<const uint16_t*>(sh.kv);
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const int dv = 128 * wave + 16 * nt + c;
+    for (int nt = 0; nt < 4; ++nt) {
+      const int col = 8 * wave + 2 * nt + (c >> 3);    // 16-byte chunk of value column 64w + 16nt + c
       u16x8 v;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        v[jj] = kv16[(4 * g + jj) * (kLdsRowStride / 2) + dv];
-        v[4 + jj] = kv16[(16 + 4 * g + jj) * (kLdsRowStride / 2) + dv];
-      }
+      for (int jj = 0; jj < 8; ++jj)
+        v[jj] = *reinterpret_cast<const uint16_t*>(kvt + v_row[jj] + ((col ^ v_sw[jj]) << 4));
       const bf16x8 vb = __builtin_bit_cast(bf16x8, v);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) acc_o[mt][nt] = mfma_bf16(pa[mt], vb, acc_o[mt][nt]);
     }
-    __syncthreads();
-    if (tile + 1 < n_tiles) store_tile();
-    __syncthreads();
   }
 
   // ---- finish: denominators, lse, normalized output ----
-  float l = l_part;
-  l += shfl_xor_f(l, 16);
-  l += shfl_xor_f(l, 32);
-  const int hq = head0 + 16 * wave + c;     // head of this lane in the score layout
-  const float lse_val = (l > 0.f) ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
-  if (g == 0) {
-    sh.lsum[16 * wave + c] = l;
-    if (S == 1) {
-      if (p.lse) p.lse[(int64_t)t * Hm + hq] = lse_val;
-    } else {
-      p.part_lse[((int64_t)t * S + s) * Hm + hq] = lse_val;
+  if (kh == 0) {
+    const float l = sum_over_groups(l_part);
+    const int hq = head0 + 16 * ht + c;     // head of this lane in the score layout
+    const float lse_val = (l > 0.f) ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
+    if (g == 0) {
+      sh.lsum[16 * ht + c] = l;
+      if (S == 1) {
+        if (p.lse) p.lse[(int64_t)t * Hm + hq] = lse_val;
+      } else {
+        p.part_lse[((int64_t)t * S + s) * Hm + hq] = lse_val;
+      }
     }
   }
   __syncthreads();
@@ -301,12 +400,12 @@ __global__ __launch_bounds__(kMlaThreads, 1) void mla_bf16_kernel(MlaParams p) {
       if (S == 1) {
         uint16_t* orow = static_cast<uint16_t*>(p.out) + ((int64_t)t * Hm + h) * kMlaDl;
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
-          orow[128 * wave + 16 * nt + c] = f32_to_bf16_bits(acc_o[mt][nt][i] * inv);
+        for (int nt = 0; nt < 4; ++nt)
+          orow[64 * wave + 16 * nt + c] = f32_to_bf16_bits(acc_o[mt][nt][i] * inv);
       } else {
         float* orow = p.part_o + (((int64_t)t * S + s) * Hm + h) * kMlaDl;
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) orow[128 * wave + 16 * nt + c] = acc_o[mt][nt][i] * inv;
+        for (int nt = 0; nt < 4; ++nt) orow[64 * wave + 16 * nt + c] = acc_o[mt][nt][i] * inv;
       }
     }
   }
