@@ -50,6 +50,8 @@ constexpr int kChunksPerRow = kRowBytes / 16;           // 72 chunks of 16 bytes
 constexpr int kTileBytes = kMlaTile * kRowBytes;        // 36864
 constexpr int kDmaPerTile = kTileBytes / 1024;          // 36 wave-wide 1 KB copies
 constexpr int kRing = 3;                                // tiles resident: 1 computing, 2 landing
+constexpr int kDmaWaves = kMlaWaves / 2;                // the second-half score waves issue the copies
+constexpr int kDmaPerWave = kDmaPerTile / kDmaWaves;    // 9
 constexpr int kEntriesPerThread = kMlaMaxEntriesPerBlock / kMlaThreads;  // 4
 constexpr int kKSteps = kMlaDqk / 2 / 32;               // 9 K-steps of 32 in each half of 576
 constexpr int kPRow = kMlaTile + 4;                     // P row stride (72 B): conflict-free rows
@@ -58,6 +60,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 
 struct MlaShared {
@@ -209,28 +213,31 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
   const uint8_t* kvbase = static_cast<const uint8_t*>(p.kv);
   const int n_tiles = (nvalid + kMlaTile - 1) / kMlaTile;
 
-  // one tile = 36 wave-wide 1 KB copies; wave w issues copies w, w+8, ... (waves
-  // 0-3 issue five, waves 4-7 four). Copy i fills LDS chunks 64i .. 64i+63.
-  auto issue_tile = [&](int tile) {
-    uint8_t* dst = sh.kv[tile % kRing];
-    const uint8_t* src[5];
+  // One tile = 36 wave-wide 1 KB copies, issued by the four second-half score
+  // waves (which have no softmax to run): wave 4 + j issues copies j, j + 4, ...
+  // Copy i fills LDS chunks 64i .. 64i+63; the row and logical column of each
+  // lane's chunk do not depend on the tile.
+  int dma_row[kDmaPerWave], dma_col[kDmaPerWave];
 #pragma unroll
-    for (int q = 0; q < 5; ++q) {                       // row ids first (LDS reads) ...
-      const int i = wave + kMlaWaves * q;
-      const int chunk = 64 * i + lane;
-      const int r = chunk / kChunksPerRow;
-      const int posc = chunk % kChunksPerRow;
-      const int col = posc ^ swz(r);                    // logical chunk stored at posc
-      const int e = tile * kMlaTile + r;
+  for (int q = 0; q < kDmaPerWave; ++q) {
+    const int i = (wave & 3) + kDmaWaves * q;
+    const int chunk = 64 * i + lane;
+    const int r = chunk / kChunksPerRow;
+    dma_row[q] = r;
+    dma_col[q] = ((chunk % kChunksPerRow) ^ swz(r)) * 16;   // logical chunk stored at this position
+  }
+  auto issue_tile = [&](int tile) {                     // second-half waves only
+    const uint32_t dst = lds_offset(sh.kv[tile % kRing]);
+    int64_t rid[kDmaPerWave];
+#pragma unroll
+    for (int q = 0; q < kDmaPerWave; ++q) {             // row ids first (LDS reads) ...
+      const int e = tile * kMlaTile + dma_row[q];
       // rows past the end re-read the split's first row; their scores are masked
-      const int64_t rid = (i < kDmaPerTile) ? sh.rowid[e < nvalid ? e : 0] : 0;
-      src[q] = kvbase + rid * kRowBytes + col * 16;
+      rid[q] = sh.rowid[e < nvalid ? e : 0];
     }
 #pragma unroll
-    for (int q = 0; q < 5; ++q) {                       // ... then all copies back to back
-      const int i = wave + kMlaWaves * q;
-      if (i < kDmaPerTile) lds_dma16(src[q], lds_offset(dst + 1024 * i));
-    }
+    for (int q = 0; q < kDmaPerWave; ++q)               // ... then the copies back to back
+      lds_dma16(kvbase + rid[q] * kRowBytes + dma_col[q], dst + 1024 * ((wave & 3) + kDmaWaves * q));
   };
 
   // Consume q here: the compiler then knows its loads have completed, and it
@@ -239,8 +246,10 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
 #pragma unroll
   for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" :: "v"(qf[ks]));
 
-  if (n_tiles > 0) issue_tile(0);
-  if (n_tiles > 1) issue_tile(1);
+  if (kh == 1) {
+    if (n_tiles > 0) issue_tile(0);
+    if (n_tiles > 1) issue_tile(1);
+  }
 
   f32x4 acc_o[4][4];   // O[heads 16mt + 4g + i][value column 64*wave + 16nt + c]
 #pragma unroll
@@ -264,10 +273,8 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
   }
 
   // tile 0 visible before the loop
-  if (n_tiles > 1) {
-    if (wave < 4) wait_vmcnt<5>(); else wait_vmcnt<4>();
-  } else {
-    wait_vmcnt<0>();
+  if (kh == 1) {
+    if (n_tiles > 1) wait_vmcnt<kDmaPerWave>(); else wait_vmcnt<0>();
   }
   __syncthreads();
 
@@ -298,7 +305,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
       sh.sx[ht][1][lane] = own1;
     }
     __syncthreads();                                     // barrier B
-    if (tile + 2 < n_tiles) issue_tile(tile + 2);       // slot of tile - 1: free after B
+    if (kh == 1 && tile + 2 < n_tiles) issue_tile(tile + 2);   // slot of tile - 1: free after B
 
     if (kh == 0) {
       const f32x4 sc0 = own0 + sh.sx[ht][0][lane];
@@ -308,8 +315,15 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
       float sv[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sv[i] = (rowbase + 4 * g + i < nvalid) ? sc0[i] * scale_log2 : -INFINITY;
-        sv[4 + i] = (rowbase + 16 + 4 * g + i < nvalid) ? sc1[i] * scale_log2 : -INFINITY;
+        sv[i] = sc0[i] * scale_log2;
+        sv[4 + i] = sc1[i] * scale_log2;
+      }
+      if (rowbase + kMlaTile > nvalid) {                 // only the last tile has padding rows
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sv[i] = (rowbase + 4 * g + i < nvalid) ? sv[i] : -INFINITY;
+          sv[4 + i] = (rowbase + 16 + 4 * g + i < nvalid) ? sv[4 + i] : -INFINITY;
+        }
       }
       float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                        fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
@@ -321,25 +335,25 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
         l_part *= alpha;
       }
       if (__ballot(alpha != 1.f) != 0ull && lane == 0) sh.flag[tile & 1] = 1;
-      uint16_t pb[8];
+      float pr[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float pr = __builtin_amdgcn_exp2f(sv[i] - m_ref);
-        l_part += pr;
-        pb[i] = f32_to_bf16_bits(pr);
+        pr[i] = __builtin_amdgcn_exp2f(sv[i] - m_ref);
+        l_part += pr[i];
       }
+      bf16x2 pb[4];                                      // round to nearest even (v_cvt_pk_bf16_f32)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pb[i] = __builtin_convertvector(f32x2{pr[2 * i], pr[2 * i + 1]}, bf16x2);
       uint16_t* prow = sh.pbuf + (16 * ht + c) * kPRow;
-      *reinterpret_cast<u16x4*>(prow + 4 * g) = u16x4{pb[0], pb[1], pb[2], pb[3]};
-      *reinterpret_cast<u16x4*>(prow + 16 + 4 * g) = u16x4{pb[4], pb[5], pb[6], pb[7]};
+      *reinterpret_cast<bf16x2*>(prow + 4 * g) = pb[0];
+      *reinterpret_cast<bf16x2*>(prow + 4 * g + 2) = pb[1];
+      *reinterpret_cast<bf16x2*>(prow + 16 + 4 * g) = pb[2];
+      *reinterpret_cast<bf16x2*>(prow + 16 + 4 * g + 2) = pb[3];
       if (g == 0) sh.alpha[16 * ht + c] = alpha;
     }
     // tile + 1 has landed once at most tile + 2's copies are pending
-    if (tile + 1 < n_tiles) {
-      if (tile + 2 < n_tiles) {
-        if (wave < 4) wait_vmcnt<5>(); else wait_vmcnt<4>();
-      } else {
-        wait_vmcnt<0>();
-      }
+    if (kh == 1 && tile + 1 < n_tiles) {
+      if (tile + 2 < n_tiles) wait_vmcnt<kDmaPerWave>(); else wait_vmcnt<0>();
     }
     __syncthreads();                                     // barrier C
 
@@ -412,30 +426,34 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
 }
 
 // LSE merge of the split partials (merge_attn_states generalised to S parts).
+// 256 threads cover two heads of one row; each thread owns four value columns.
 template <bool kBf16Out>
-__global__ __launch_bounds__(128) void mla_combine_kernel(MlaParams p) {
-  const int t = blockIdx.x, h = blockIdx.y;
+__global__ __launch_bounds__(256) void mla_combine_kernel(MlaParams p) {
+  const int t = blockIdx.x;
+  const int h = 2 * blockIdx.y + (threadIdx.x >> 7);
+  const int d4 = threadIdx.x & 127;                 // value columns 4*d4 .. 4*d4+3
   const int S = p.splits, Hm = p.heads, Dl = p.d_latent;
+  if (h >= Hm || 4 * d4 >= Dl) return;
   const float* pl = p.part_lse + (int64_t)t * S * Hm + h;
   float mx = -INFINITY;
   for (int s = 0; s < S; ++s) mx = fmaxf(mx, pl[(int64_t)s * Hm]);
   float tot = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < S; ++s) {
-    const float v = pl[(int64_t)s * Hm];
-    tot += (v == -INFINITY) ? 0.f : expf(v - mx);
+    const float l = pl[(int64_t)s * Hm];
+    const float wgt = (l == -INFINITY) ? 0.f : __expf(l - mx);
+    tot += wgt;
+    const f32x4 o = *reinterpret_cast<const f32x4*>(p.part_o + (((int64_t)t * S + s) * Hm + h) * Dl + 4 * d4);
+    acc += wgt * o;
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
-  if (threadIdx.x == 0 && p.lse) p.lse[(int64_t)t * Hm + h] = tot > 0.f ? mx + logf(tot) : -INFINITY;
-  for (int d = threadIdx.x; d < Dl; d += blockDim.x) {
-    float acc = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float v = pl[(int64_t)s * Hm];
-      if (v == -INFINITY) continue;
-      acc += expf(v - mx) * p.part_o[(((int64_t)t * S + s) * Hm + h) * Dl + d];
-    }
-    acc *= inv;
-    if (kBf16Out) static_cast<uint16_t*>(p.out)[((int64_t)t * Hm + h) * Dl + d] = f32_to_bf16_bits(acc);
-    else static_cast<float*>(p.out)[((int64_t)t * Hm + h) * Dl + d] = acc;
+  acc *= inv;
+  if (d4 == 0 && p.lse) p.lse[(int64_t)t * Hm + h] = tot > 0.f ? mx + __logf(tot) : -INFINITY;
+  if (kBf16Out) {
+    const bf16x4 o = __builtin_convertvector(acc, bf16x4);
+    *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(p.out) + ((int64_t)t * Hm + h) * Dl + 4 * d4) = o;
+  } else {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + ((int64_t)t * Hm + h) * Dl + 4 * d4) = acc;
   }
 }
 
@@ -522,7 +540,8 @@ int mla_bf16_splits(int num_rows, int k, int heads) {
   const int groups = num_rows * (heads / kMlaHeadsPerGroup);
   if (groups <= 0) return 1;
   const int min_splits = (k + kMlaMaxEntriesPerBlock - 1) / kMlaMaxEntriesPerBlock;
-  const int max_splits = (k + 2 * kMlaTile - 1) / (2 * kMlaTile);   // >= 2 tiles per split
+  int max_splits = (k + 2 * kMlaTile - 1) / (2 * kMlaTile);         // >= 2 tiles per split
+  if (max_splits > 16) max_splits = 16;
   int sp = (256 + groups - 1) / groups;
   if (sp > max_splits) sp = max_splits;
   if (sp < min_splits) sp = min_splits;
@@ -546,7 +565,7 @@ hipError_t launch_mla_bf16(const MlaParams& p, hipStream_t s) {
   hipLaunchKernelGGL(mla_bf16_kernel, dim3((unsigned)blocks), dim3(kMlaThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  hipLaunchKernelGGL(mla_combine_kernel<true>, dim3(T, p.heads), dim3(128), 0, s, p);
+  hipLaunchKernelGGL(mla_combine_kernel<true>, dim3(T, (p.heads + 1) / 2), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
