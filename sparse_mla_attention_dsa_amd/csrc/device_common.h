@@ -68,4 +68,20 @@ __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
   return __shfl_xor(v, mask, kWave);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave, on DPP lane moves (no LDS
+// round trip): shifts of 1, 2, 4, 8 lanes inside each 16-lane row, then the
+// last lane of row 0 / row 2 is added to rows 1 / 3, and the last lane of
+// row 1 to rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+  // dpp_ctrl: row_shr:n = 0x110 + n, row_bcast:15 = 0x142, row_bcast:31 = 0x143;
+  // bound_ctrl = true makes lanes without a source read 0.
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);
+  return v;
+}
+
 }  // namespace dsa

@@ -48,10 +48,9 @@ constexpr int kMlaWaves = kMlaThreads / kWave;          // 8
 constexpr int kRowBytes = kMlaDqk * 2;                  // 1152: one cached latent row
 constexpr int kChunksPerRow = kRowBytes / 16;           // 72 chunks of 16 bytes
 constexpr int kTileBytes = kMlaTile * kRowBytes;        // 36864
-constexpr int kDmaPerTile = kTileBytes / 1024;          // 36 wave-wide 1 KB copies
-constexpr int kRing = 3;                                // tiles resident: 1 computing, 2 landing
-constexpr int kDmaWaves = kMlaWaves / 2;                // the second-half score waves issue the copies
-constexpr int kDmaPerWave = kDmaPerTile / kDmaWaves;    // 9
+constexpr int kDmaPerTile = kTileBytes / 1024;          // 36 wave-wide 1 KB pieces
+constexpr int kRing = 3;                                // LDS tile slots
+constexpr int kCopies = 5;                              // 16-byte copies per thread per tile (36 per wave-slot)
 constexpr int kEntriesPerThread = kMlaMaxEntriesPerBlock / kMlaThreads;  // 4
 constexpr int kKSteps = kMlaDqk / 2 / 32;               // 9 K-steps of 32 in each half of 576
 constexpr int kPRow = kMlaTile + 4;                     // P row stride (72 B): conflict-free rows
@@ -69,9 +68,9 @@ struct MlaShared {
   // stored at chunk position c ^ swz(r) (see swz).
   alignas(16) uint8_t kv[kRing][kTileBytes];
   int32_t rowid[kMlaMaxEntriesPerBlock];
-  alignas(16) uint16_t pbuf[kMlaHeadsPerGroup * kPRow];     // [head][row] bf16 bits, padded rows
+  alignas(16) uint16_t pbuf[2][kMlaHeadsPerGroup * kPRow];  // [parity][head][row] bf16, padded rows
   alignas(16) f32x4 sx[kMlaWaves / 2][2][kWave];            // second-half partial scores
-  alignas(16) float alpha[kMlaHeadsPerGroup];
+  alignas(16) float alpha[2][kMlaHeadsPerGroup];
   alignas(16) float lsum[kMlaHeadsPerGroup];
   int flag[2];
   int wave_sum[kMlaWaves];
@@ -104,22 +103,6 @@ __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, con
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Copy 16 bytes per lane from global memory straight into LDS: lane l's bytes
-// land at LDS offset lds_off + 16 * l (wave-uniform lds_off). M0 is set here
-// explicitly; completion is tracked with vmcnt by the caller.
-__device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t lds_off) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(gsrc), "s"(lds_off) : "memory", "m0");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_offset(const void* p) {
-  return (uint32_t)reinterpret_cast<uintptr_t>(p);   // LDS aperture: low 32 bits are the offset
-}
 
 __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
   __shared__ MlaShared sh;
@@ -213,31 +196,40 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
   const uint8_t* kvbase = static_cast<const uint8_t*>(p.kv);
   const int n_tiles = (nvalid + kMlaTile - 1) / kMlaTile;
 
-  // One tile = 36 wave-wide 1 KB copies, issued by the four second-half score
-  // waves (which have no softmax to run): wave 4 + j issues copies j, j + 4, ...
-  // Copy i fills LDS chunks 64i .. 64i+63; the row and logical column of each
-  // lane's chunk do not depend on the tile.
-  int dma_row[kDmaPerWave], dma_col[kDmaPerWave];
+  // A tile is 36 pieces of 1 KB; piece i holds LDS chunks 64i .. 64i+63 and is
+  // fetched by wave i % 8 (waves 0-3 fetch five pieces, waves 4-7 four), lane l
+  // taking chunk 64i + l: the logical chunk col ^ swz(row) of its row goes to
+  // LDS position col. The pieces of a tile travel global -> VGPR -> LDS.
+  int cp_row[kCopies], cp_col[kCopies];
 #pragma unroll
-  for (int q = 0; q < kDmaPerWave; ++q) {
-    const int i = (wave & 3) + kDmaWaves * q;
+  for (int q = 0; q < kCopies; ++q) {
+    const int i = min(wave + kMlaWaves * q, kDmaPerTile - 1);
     const int chunk = 64 * i + lane;
     const int r = chunk / kChunksPerRow;
-    dma_row[q] = r;
-    dma_col[q] = ((chunk % kChunksPerRow) ^ swz(r)) * 16;   // logical chunk stored at this position
+    cp_row[q] = r;
+    cp_col[q] = ((chunk % kChunksPerRow) ^ swz(r)) * 16;
   }
-  auto issue_tile = [&](int tile) {                     // second-half waves only
-    const uint32_t dst = lds_offset(sh.kv[tile % kRing]);
-    int64_t rid[kDmaPerWave];
+  const bool five = wave + kMlaWaves * (kCopies - 1) < kDmaPerTile;   // wave-uniform
+  auto load_tile = [&](int tile, i32x4 (&st)[kCopies]) {
+    if (tile >= n_tiles) return;
+    int64_t rid[kCopies];
 #pragma unroll
-    for (int q = 0; q < kDmaPerWave; ++q) {             // row ids first (LDS reads) ...
-      const int e = tile * kMlaTile + dma_row[q];
-      // rows past the end re-read the split's first row; their scores are masked
-      rid[q] = sh.rowid[e < nvalid ? e : 0];
+    for (int q = 0; q < kCopies; ++q) {
+      const int e = tile * kMlaTile + cp_row[q];
+      rid[q] = sh.rowid[e < nvalid ? e : 0];   // rows past the end re-read the split's first row (masked)
     }
 #pragma unroll
-    for (int q = 0; q < kDmaPerWave; ++q)               // ... then the copies back to back
-      lds_dma16(kvbase + rid[q] * kRowBytes + dma_col[q], dst + 1024 * ((wave & 3) + kDmaWaves * q));
+    for (int q = 0; q < kCopies - 1; ++q)
+      st[q] = *reinterpret_cast<const i32x4*>(kvbase + rid[q] * kRowBytes + cp_col[q]);
+    if (five) st[kCopies - 1] = *reinterpret_cast<const i32x4*>(kvbase + rid[kCopies - 1] * kRowBytes + cp_col[kCopies - 1]);
+  };
+  auto store_tile = [&](int tile, const i32x4 (&st)[kCopies]) {
+    if (tile >= n_tiles) return;
+    uint8_t* dst = sh.kv[tile % kRing] + 16 * lane;
+#pragma unroll
+    for (int q = 0; q < kCopies - 1; ++q)
+      *reinterpret_cast<i32x4*>(dst + 1024 * (wave + kMlaWaves * q)) = st[q];
+    if (five) *reinterpret_cast<i32x4*>(dst + 1024 * (wave + kMlaWaves * (kCopies - 1))) = st[kCopies - 1];
   };
 
   // Consume q here: the compiler then knows its loads have completed, and it
@@ -246,10 +238,6 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
 #pragma unroll
   for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" :: "v"(qf[ks]));
 
-  if (kh == 1) {
-    if (n_tiles > 0) issue_tile(0);
-    if (n_tiles > 1) issue_tile(1);
-  }
 
   f32x4 acc_o[4][4];   // O[heads 16mt + 4g + i][value column 64*wave + 16nt + c]
 #pragma unroll
@@ -272,19 +260,10 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
     v_sw[jj] = swz(r);
   }
 
-  // tile 0 visible before the loop
-  if (kh == 1) {
-    if (n_tiles > 1) wait_vmcnt<kDmaPerWave>(); else wait_vmcnt<0>();
-  }
-  __syncthreads();
-
-  // Per tile: scores -> [barrier B] -> copies of tile + 2, softmax, wait for
-  // tile + 1 -> [barrier C] -> P.V. Barrier B also guarantees that every wave
-  // has finished P.V of the previous tile, so its ring slot can be refilled.
-  for (int tile = 0; tile < n_tiles; ++tile) {
+  // ---- helpers of the pipelined loop ----
+  // partial scores of `tile` over this wave's half of the contraction
+  auto scores = [&](int tile, f32x4& own0, f32x4& own1) {
     const uint8_t* kvt = sh.kv[tile % kRing];
-
-    // ---- partial scores: 32 rows x 16 heads over this wave's half ----
     f32x4 sa0 = {0.f, 0.f, 0.f, 0.f}, sa1 = sa0, sb0 = sa0, sb1 = sa0;
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
@@ -299,14 +278,66 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
         sa1 = mfma_bf16(a1, qf[ks], sa1);
       }
     }
-    const f32x4 own0 = sa0 + sb0, own1 = sa1 + sb1;
+    own0 = sa0 + sb0;
+    own1 = sa1 + sb1;
     if (kh == 1) {
       sh.sx[ht][0][lane] = own0;
       sh.sx[ht][1][lane] = own1;
     }
-    __syncthreads();                                     // barrier B
-    if (kh == 1 && tile + 2 < n_tiles) issue_tile(tile + 2);   // slot of tile - 1: free after B
+  };
+  // O[64 heads x value columns 64w..64w+63] += P(tile) . V(tile), after the rescale
+  auto pv = [&](int tile) {
+    const int par = tile & 1;
+    const uint8_t* kvt = sh.kv[tile % kRing];
+    if (sh.flag[par]) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(sh.alpha[par] + 16 * mt + 4 * g);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc_o[mt][nt] *= a4;
+      }
+    }
+    bf16x8 pa[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const uint16_t* pr = sh.pbuf[par] + (16 * mt + c) * kPRow;
+      const u16x4 lo = *reinterpret_cast<const u16x4*>(pr + 4 * g);
+      const u16x4 hi = *reinterpret_cast<const u16x4*>(pr + 16 + 4 * g);
+      const u16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      pa[mt] = __builtin_bit_cast(bf16x8, v);
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int col = 8 * wave + 2 * nt + (c >> 3);    // 16-byte chunk of value column 64w + 16nt + c
+      u16x8 v;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj)
+        v[jj] = *reinterpret_cast<const uint16_t*>(kvt + v_row[jj] + ((col ^ v_sw[jj]) << 4));
+      const bf16x8 vb = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc_o[mt][nt] = mfma_bf16(pa[mt], vb, acc_o[mt][nt]);
+    }
+  };
 
+  // Software pipeline, one tile deep: iteration j overlaps the softmax of tile j
+  // (VALU, first-half waves) with P.V of tile j - 1 (MFMA, all waves), stores
+  // tile j + 1 (fetched one iteration earlier) into the slot of tile j - 2 and
+  // fetches tile j + 2; after barrier C it computes the scores of tile j + 1,
+  // and barrier B makes the score halves visible. P, the rescale factors and
+  // the rescale flag are double-buffered by tile parity.
+  i32x4 st[kCopies];
+  f32x4 own0 = {0.f, 0.f, 0.f, 0.f}, own1 = own0;
+  if (n_tiles > 0) {
+    load_tile(0, st);
+    store_tile(0, st);
+    load_tile(1, st);
+    __syncthreads();                                     // tile 0 visible
+    scores(0, own0, own1);
+    __syncthreads();                                     // barrier B of tile 0
+  }
+  // st holds tile + 1 (in flight)
+  auto step = [&](int tile, i32x4 (&X)[kCopies]) {
+    const int par = tile & 1;
     if (kh == 0) {
       const f32x4 sc0 = own0 + sh.sx[ht][0][lane];
       const f32x4 sc1 = own1 + sh.sx[ht][1][lane];
@@ -334,7 +365,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
         m_ref = mx;
         l_part *= alpha;
       }
-      if (__ballot(alpha != 1.f) != 0ull && lane == 0) sh.flag[tile & 1] = 1;
+      if (__ballot(alpha != 1.f) != 0ull && lane == 0) sh.flag[par] = 1;
       float pr[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -344,50 +375,25 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
       bf16x2 pb[4];                                      // round to nearest even (v_cvt_pk_bf16_f32)
 #pragma unroll
       for (int i = 0; i < 4; ++i) pb[i] = __builtin_convertvector(f32x2{pr[2 * i], pr[2 * i + 1]}, bf16x2);
-      uint16_t* prow = sh.pbuf + (16 * ht + c) * kPRow;
+      uint16_t* prow = sh.pbuf[par] + (16 * ht + c) * kPRow;
       *reinterpret_cast<bf16x2*>(prow + 4 * g) = pb[0];
       *reinterpret_cast<bf16x2*>(prow + 4 * g + 2) = pb[1];
       *reinterpret_cast<bf16x2*>(prow + 16 + 4 * g) = pb[2];
       *reinterpret_cast<bf16x2*>(prow + 16 + 4 * g + 2) = pb[3];
-      if (g == 0) sh.alpha[16 * ht + c] = alpha;
+      if (g == 0) sh.alpha[par][16 * ht + c] = alpha;
     }
-    // tile + 1 has landed once at most tile + 2's copies are pending
-    if (kh == 1 && tile + 1 < n_tiles) {
-      if (tile + 2 < n_tiles) wait_vmcnt<kDmaPerWave>(); else wait_vmcnt<0>();
-    }
+    if (tile > 0) pv(tile - 1);
+    store_tile(tile + 1, X);                             // slot of tile - 2: free since barrier C of tile - 1
+    load_tile(tile + 2, X);
     __syncthreads();                                     // barrier C
-
-    // ---- O[64 heads x value columns 64w..64w+63] += P . V ----
-    if (sh.flag[tile & 1]) {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const f32x4 a4 = *reinterpret_cast<const f32x4*>(sh.alpha + 16 * mt + 4 * g);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc_o[mt][nt] *= a4;
-      }
+    if (tid == 0) sh.flag[par ^ 1] = 0;                  // next used by the softmax of tile + 1
+    if (tile + 1 < n_tiles) {
+      scores(tile + 1, own0, own1);
+      __syncthreads();                                   // barrier B of tile + 1
     }
-    if (tid == 0) sh.flag[(tile + 1) & 1] = 0;
-    bf16x8 pa[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const uint16_t* pr = sh.pbuf + (16 * mt + c) * kPRow;
-      const u16x4 lo = *reinterpret_cast<const u16x4*>(pr + 4 * g);
-      const u16x4 hi = *reinterpret_cast<const u16x4*>(pr + 16 + 4 * g);
-      const u16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      pa[mt] = __builtin_bit_cast(bf16x8, v);
-    }
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int col = 8 * wave + 2 * nt + (c >> 3);    // 16-byte chunk of value column 64w + 16nt + c
-      u16x8 v;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj)
-        v[jj] = *reinterpret_cast<const uint16_t*>(kvt + v_row[jj] + ((col ^ v_sw[jj]) << 4));
-      const bf16x8 vb = __builtin_bit_cast(bf16x8, v);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) acc_o[mt][nt] = mfma_bf16(pa[mt], vb, acc_o[mt][nt]);
-    }
-  }
+  };
+  for (int tile = 0; tile < n_tiles; ++tile) step(tile, st);
+  if (n_tiles > 0) pv(n_tiles - 1);
 
   // ---- finish: denominators, lse, normalized output ----
   if (kh == 0) {

@@ -29,10 +29,13 @@ constexpr int kTkCache = 32768;
 constexpr int kTkBins = 4096;
 constexpr int kTkLoadUnroll = 16;          // float4 loads in flight per thread
 constexpr int kTkPer = 8;                  // consecutive positions per thread per pass step
+constexpr int kTkCand = 4032;              // keys sharing the top 12 bits kept for the last level
 
 struct TopkShared {
   uint32_t hist[kTkBins];
   alignas(16) uint32_t keys[kTkCache];
+  uint32_t cand[kTkCand];
+  uint32_t n_cand;
   uint32_t wave_sum[2][kTkWaves];
   uint32_t sel_bin;
   uint32_t sel_above;
@@ -62,12 +65,7 @@ __device__ __forceinline__ void load8(const float* __restrict__ row, const TopkS
 // the double-buffered wave totals so consecutive calls need no extra barrier.
 __device__ __forceinline__ uint32_t block_scan(TopkShared& sh, uint32_t v, int buf, uint32_t* total) {
   const int lane = lane_id(), wave = wave_id();
-  uint32_t incl = v;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const uint32_t o = __shfl_up(incl, d, kWave);
-    if (lane >= d) incl += o;
-  }
+  const uint32_t incl = wave_inclusive_scan(v);
   if (lane == kWave - 1) sh.wave_sum[buf][wave] = incl;
   __syncthreads();
   uint32_t before = 0, tot = 0;
@@ -175,15 +173,22 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
   uint32_t prefix = bin;
   need -= above;
 
-  // ---- level 1 (bits 19..8) among keys whose top 12 bits equal the prefix ----
+  // ---- level 1 (bits 19..8) among keys whose top 12 bits equal the prefix;
+  //      those keys are also collected (unordered) for the last level ----
+  const bool keep = sh.hist[prefix] <= (uint32_t)kTkCand;   // read before the histogram is cleared
+  __syncthreads();
   for (int i = tid; i < kTkBins; i += kTkThreads) sh.hist[i] = 0;
+  if (tid == 0) sh.n_cand = 0;
   __syncthreads();
   for (int i = kTkPer * tid; i < n; i += kTkPer * kTkThreads) {
     uint32_t u[kTkPer];
     load8(row, sh, cached, n, i, u);
 #pragma unroll
     for (int e = 0; e < kTkPer; ++e)
-      if (i + e < n && (u[e] >> 20) == prefix) atomicAdd(&sh.hist[(u[e] >> 8) & 0xfffu], 1u);
+      if (i + e < n && (u[e] >> 20) == prefix) {
+        atomicAdd(&sh.hist[(u[e] >> 8) & 0xfffu], 1u);
+        if (keep) sh.cand[atomicAdd(&sh.n_cand, 1u)] = u[e];
+      }
   }
   __syncthreads();
   select_bin(sh, kTkBins, need, 1, &bin, &above);
@@ -193,12 +198,20 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
   // ---- level 2 (bits 7..0) among keys whose top 24 bits equal the prefix ----
   for (int i = tid; i < 256; i += kTkThreads) sh.hist[i] = 0;
   __syncthreads();
-  for (int i = kTkPer * tid; i < n; i += kTkPer * kTkThreads) {
-    uint32_t u[kTkPer];
-    load8(row, sh, cached, n, i, u);
+  if (keep) {
+    const uint32_t nc = sh.n_cand;
+    for (uint32_t i = tid; i < nc; i += kTkThreads) {
+      const uint32_t u = sh.cand[i];
+      if ((u >> 8) == prefix) atomicAdd(&sh.hist[u & 0xffu], 1u);
+    }
+  } else {
+    for (int i = kTkPer * tid; i < n; i += kTkPer * kTkThreads) {
+      uint32_t u[kTkPer];
+      load8(row, sh, cached, n, i, u);
 #pragma unroll
-    for (int e = 0; e < kTkPer; ++e)
-      if (i + e < n && (u[e] >> 8) == prefix) atomicAdd(&sh.hist[u[e] & 0xffu], 1u);
+      for (int e = 0; e < kTkPer; ++e)
+        if (i + e < n && (u[e] >> 8) == prefix) atomicAdd(&sh.hist[u[e] & 0xffu], 1u);
+    }
   }
   __syncthreads();
   select_bin(sh, 256, need, 0, &bin, &above);
@@ -229,24 +242,26 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
     uint32_t total;
     const uint32_t packed = (cgt << 16) | ceq;
     const uint32_t excl = block_scan(sh, packed, it & 1, &total) - packed;
+    // winner e goes to (#gt before it) + min(#eq before it, need); the same
+    // formula covers both kinds because a taken tie has #eq before it < need
     uint32_t gt_before = base_gt + (excl >> 16);
     uint32_t eq_before = base_eq + (excl & 0xffffu);
     if (packed) {
+      uint32_t pos[kTkPer];
+      bool take[kTkPer];
 #pragma unroll
       for (int e = 0; e < kTkPer; ++e) {
         const bool valid = i + e < n;
-        if (valid && u[e] > thr) {
-          const uint32_t pos = gt_before + (eq_before < need ? eq_before : need);
-          if (pos < (uint32_t)k) out[pos] = i + e;
-          ++gt_before;
-        } else if (valid && u[e] == thr) {
-          if (eq_before < need) {
-            const uint32_t pos = gt_before + eq_before;
-            if (pos < (uint32_t)k) out[pos] = i + e;
-          }
-          ++eq_before;
-        }
+        const bool isgt = valid && u[e] > thr;
+        const bool iseq = valid && u[e] == thr;
+        take[e] = isgt || (iseq && eq_before < need);
+        pos[e] = gt_before + (eq_before < need ? eq_before : need);
+        gt_before += isgt ? 1u : 0u;
+        eq_before += iseq ? 1u : 0u;
       }
+#pragma unroll
+      for (int e = 0; e < kTkPer; ++e)
+        if (take[e] && pos[e] < (uint32_t)k) out[pos[e]] = i + e;
     }
     base_gt += total >> 16;
     base_eq += total & 0xffffu;
