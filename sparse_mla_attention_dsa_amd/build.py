@@ -29,6 +29,15 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-source code generation options. The sparse attention kernel keeps its
+# output accumulator in VGPRs (its rare rescale is VALU work on it) while q
+# lives in AGPRs, and its LDS reads are scheduled as clauses ahead of the MFMAs.
+SOURCE_FLAGS = {
+    "sparse_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1",
+                       "-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
+}
+
+
 def _hipcc():
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):
@@ -39,7 +48,8 @@ def _hipcc():
 def _compile(src, extra):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [_hipcc()] + COMMON_FLAGS + extra + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ([_hipcc()] + COMMON_FLAGS + SOURCE_FLAGS.get(src, []) + extra + lang +
+           ["-c", os.path.join(CSRC, src), "-o", obj])
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compiling {src} failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")

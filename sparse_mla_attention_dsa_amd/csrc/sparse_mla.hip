@@ -10,28 +10,32 @@
 //   z_i = scale * (q[t,h] . C_i),  out[t,h] = sum_i softmax(z)_i C_i[:512],
 //   lse[t,h] = log sum_i exp(z_i).
 //
-// bf16 path (Dl = 512, Dr = 64, Hm a multiple of 64). One work-group of eight
-// waves handles one (row, split of the top-k list, group of 64 heads):
+// bf16 path (Dl = 512, Dr = 64, Hm a multiple of 64). One work-group of four
+// waves (one per SIMD) handles one (row, split of the top-k list, group of 64
+// heads); wave w owns heads 16w .. 16w+15 of the group outright, so scores,
+// softmax and P.V of those heads never leave the wave:
 //   * the split's positions are resolved once through the block table into
 //     cache-row ids in LDS, skipping -1 / out-of-range entries (so the -1 tail
 //     of short rows costs nothing);
-//   * gathered rows arrive 32 at a time straight from HBM into a ring of three
-//     LDS tiles (global_load_lds, 16 bytes per lane): two tiles are in flight
-//     while the third is computed on. Rows are stored dense with an XOR swizzle
-//     of their 16-byte chunks so that both LDS read patterns below are free of
-//     bank conflicts;
-//   * scores: waves w and w + 4 compute S^T[32 rows x 16 heads] = C_tile . Q^T
-//     over the two halves of the 576-wide contraction with
-//     v_mfma_f32_16x16x32_bf16 (rows = M from LDS, heads = N from registers:
-//     each wave keeps its 16 heads x 288 of q in VGPRs) and exchange the
-//     halves through LDS;
+//   * gathered rows arrive 32 at a time straight from HBM into a ring of four
+//     LDS tiles (global_load_lds, 16 bytes per lane, no register staging); two
+//     tiles are in flight while one is scored and the previous one multiplied
+//     into the output. Rows are stored dense with an XOR swizzle of their
+//     16-byte chunks, which keeps both LDS read patterns below free of bank
+//     conflicts;
+//   * scores: S^T[32 rows x 16 heads] = C_tile . Q^T over the 576-wide
+//     contraction with v_mfma_f32_16x16x32_bf16 (rows = M from LDS, heads = N:
+//     the wave keeps its 16 heads x 576 of q in registers);
 //   * online softmax in fp32, base 2, with lazy rescaling: the running maximum
 //     of a head only moves when a tile exceeds it by more than 2^8, so the
 //     accumulator rescale is skipped on most tiles;
-//   * probabilities (bf16) and the per-head rescale factors go through LDS so
-//     that wave w can compute O[64 heads x 64 value columns] += P . V_tile,
-//     again on 16x16x32 bf16 MFMA (heads = M, value columns = N). The small
-//     per-wave register footprint (q 36, O 64) gives two waves per SIMD;
+//   * the score accumulator of lane (c, g) holds head c at rows {4g+i, 16+4g+i},
+//     which is exactly the A operand (head c, eight rows of the contraction)
+//     of O[16 heads x 512] += P . V_tile, so P goes from registers to the MFMA
+//     without an LDS round trip. V arrives as the B operand through the gfx950
+//     transposing LDS read (ds_read_b64_tr_b16), two per 16 value columns;
+//   * the scores of tile j + 1 are issued before the softmax and P.V of tile j,
+//     so the wave has MFMA work while its softmax runs;
 //   * single split: out = O / l in bf16 and lse; several splits: fp32 partials
 //     (O / l, lse) merged by mla_combine_kernel.
 // Work-groups are ordered so that the head groups of one (row, split) unit, and
@@ -43,48 +47,42 @@
 namespace dsa {
 namespace {
 
-constexpr int kMlaThreads = 512;
-constexpr int kMlaWaves = kMlaThreads / kWave;          // 8
+constexpr int kMlaThreads = 256;
+constexpr int kMlaWaves = kMlaThreads / kWave;          // 4
 constexpr int kRowBytes = kMlaDqk * 2;                  // 1152: one cached latent row
 constexpr int kChunksPerRow = kRowBytes / 16;           // 72 chunks of 16 bytes
 constexpr int kTileBytes = kMlaTile * kRowBytes;        // 36864
-constexpr int kDmaPerTile = kTileBytes / 1024;          // 36 wave-wide 1 KB pieces
-constexpr int kRing = 3;                                // LDS tile slots
-constexpr int kCopies = 5;                              // 16-byte copies per thread per tile (36 per wave-slot)
-constexpr int kEntriesPerThread = kMlaMaxEntriesPerBlock / kMlaThreads;  // 4
-constexpr int kKSteps = kMlaDqk / 2 / 32;               // 9 K-steps of 32 in each half of 576
-constexpr int kPRow = kMlaTile + 4;                     // P row stride (72 B): conflict-free rows
+constexpr int kPiecesPerTile = kTileBytes / 1024;       // 36 wave-wide 1 KB copies
+constexpr int kPiecesPerWave = kPiecesPerTile / kMlaWaves;   // 9
+constexpr int kRing = 4;                                // LDS tile slots
+constexpr int kEntriesPerThread = kMlaMaxEntriesPerBlock / kMlaThreads;  // 8
+constexpr int kKSteps = kMlaDqk / 32;                   // 18 K-steps of 32
+constexpr int kVTiles = kMlaDl / 16;                    // 32 value-column tiles
 constexpr float kRescaleThreshold = 8.0f;               // log2 units
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 struct MlaShared {
   // Gathered rows, dense (1152 B per row). Inside row r the 16-byte chunk c is
   // stored at chunk position c ^ swz(r) (see swz).
   alignas(16) uint8_t kv[kRing][kTileBytes];
   int32_t rowid[kMlaMaxEntriesPerBlock];
-  alignas(16) uint16_t pbuf[2][kMlaHeadsPerGroup * kPRow];  // [parity][head][row] bf16, padded rows
-  alignas(16) f32x4 sx[kMlaWaves / 2][2][kWave];            // second-half partial scores
-  alignas(16) float alpha[2][kMlaHeadsPerGroup];
-  alignas(16) float lsum[kMlaHeadsPerGroup];
-  int flag[2];
   int wave_sum[kMlaWaves];
 };
 
-// Chunk swizzle of row r (bits 0-2 of r, bit 3 of r folded onto bits 0-1):
-// sixteen consecutive rows reading the same logical chunk, and the rows
-// {j, j+4, j+8, j+12} reading the same value column, hit distinct banks for
-// both 8-lane (128 B) and 16-lane (256 B) LDS service groups. Rows r and r + 16
-// share the swizzle.
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ (((row >> 3) & 1) * 3); }
+// Chunk swizzle of row r: the low three bits of r. With it the score operand
+// reads (sixteen rows, one logical chunk each) and the transposed value reads
+// (sixteen rows x 32 bytes) both run at the conflict-free LDS rate (measured on
+// gfx950; rows are 1152 bytes apart). Rows r and r + 16 share the swizzle.
+__device__ __forceinline__ int swz(int row) { return row & 7; }
 
-// max of v over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups), with the
-// gfx950 lane swaps (VALU, no LDS round trip)
+// max / sum of v over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups),
+// with the gfx950 lane swaps (VALU, no LDS round trip)
 __device__ __forceinline__ float max_over_groups(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
@@ -103,6 +101,29 @@ __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, con
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>(p);   // LDS aperture: low 32 bits are the offset
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at M0 + 16 l (M0 = the wave-uniform destination). Completion is counted by
+// vmcnt like any other vector load.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(gsrc), "s"(lds_addr) : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// transposing LDS read: lane 4k + m of each 16-lane block names 8 bytes (four
+// bf16) of row k; lane i of the block receives element i % 4 of lane
+// 4 * kk + i / 4's bytes in slot kk, i.e. one column of four rows
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+}
 
 __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
   __shared__ MlaShared sh;
@@ -128,8 +149,6 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(wave_id());
   const int g = lane >> 4, c = lane & 15;
-  const int ht = wave & 3;     // score role: heads 16*ht .. 16*ht+15 of the group
-  const int kh = wave >> 2;    //             half of the 576-wide contraction
 
   int b, jrow, q_len;
   row_to_seq(t, bv.cu_seqlens_q, bv.num_seqs, &b, &jrow, &q_len);
@@ -139,14 +158,8 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
   if (seq_len > addressable) seq_len = addressable;
   const int32_t* bt = bv.block_table + (int64_t)b * bv.max_pages_per_seq;
 
-  const int head0 = hg * kMlaHeadsPerGroup;
+  const int head0 = hg * kMlaHeadsPerGroup + 16 * wave;   // this wave's first head
   const int Hm = p.heads;
-  // ---- q (loads overlap the index resolution below): this wave's 16 heads, its half of the contraction (N operand) ----
-  const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
-                         ((int64_t)t * Hm + head0 + 16 * ht + c) * kMlaDqk + kh * (kMlaDqk / 2);
-  bf16x8 qf[kKSteps];
-#pragma unroll
-  for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks + 8 * g);
 
   // ---- resolve this split's entries into cache-row ids (compacted, in order) ----
   const int e_begin = s * p.entries_per_split;
@@ -165,17 +178,18 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
     const bool in = pos[q] >= 0 && pos[q] < seq_len;
     page[q] = in ? bt[pos[q] / P] : -1;
   }
+  // q (head c of the wave, all 576: the N operand) is fetched after the page
+  // lookups so that waiting for those (vector loads complete in order) does not
+  // also wait for q
+  const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + ((int64_t)t * Hm + head0 + c) * kMlaDqk;
+  bf16x8 qf[kKSteps];
+#pragma unroll
+  for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks + 8 * g);
   int nmine = 0;
 #pragma unroll
   for (int q = 0; q < kEntriesPerThread; ++q) nmine += (page[q] >= 0 && page[q] < bv.num_pages) ? 1 : 0;
-  int incl = nmine;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int o = __shfl_up(incl, d, kWave);
-    if (lane >= d) incl += o;
-  }
+  const int incl = (int)wave_inclusive_scan((uint32_t)nmine);
   if (lane == kWave - 1) sh.wave_sum[wave] = incl;
-  if (tid < 2) sh.flag[tid] = 0;
   __syncthreads();
   int nvalid = 0, w_off = 0;
 #pragma unroll
@@ -196,237 +210,230 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
   const uint8_t* kvbase = static_cast<const uint8_t*>(p.kv);
   const int n_tiles = (nvalid + kMlaTile - 1) / kMlaTile;
 
-  // A tile is 36 pieces of 1 KB; piece i holds LDS chunks 64i .. 64i+63 and is
-  // fetched by wave i % 8 (waves 0-3 fetch five pieces, waves 4-7 four), lane l
-  // taking chunk 64i + l: the logical chunk col ^ swz(row) of its row goes to
-  // LDS position col. The pieces of a tile travel global -> VGPR -> LDS.
-  int cp_row[kCopies], cp_col[kCopies];
+  // A tile is 36 copies of 1 KB; copy i = wave + 4j covers LDS chunks
+  // 64i .. 64i+63, lane l taking chunk 64i + l of the dense tile: row
+  // r = chunk / 72, LDS chunk position col = chunk % 72, which holds the
+  // logical chunk col ^ swz(r) of the row.
+  // source row ids of this wave's copies of `tile`
+  auto fetch_rows = [&](int tile, int (&rid)[kPiecesPerWave]) {
 #pragma unroll
-  for (int q = 0; q < kCopies; ++q) {
-    const int i = min(wave + kMlaWaves * q, kDmaPerTile - 1);
-    const int chunk = 64 * i + lane;
-    const int r = chunk / kChunksPerRow;
-    cp_row[q] = r;
-    cp_col[q] = ((chunk % kChunksPerRow) ^ swz(r)) * 16;
-  }
-  const bool five = wave + kMlaWaves * (kCopies - 1) < kDmaPerTile;   // wave-uniform
-  auto load_tile = [&](int tile, i32x4 (&st)[kCopies]) {
-    if (tile >= n_tiles) return;
-    int64_t rid[kCopies];
-#pragma unroll
-    for (int q = 0; q < kCopies; ++q) {
-      const int e = tile * kMlaTile + cp_row[q];
-      rid[q] = sh.rowid[e < nvalid ? e : 0];   // rows past the end re-read the split's first row (masked)
+    for (int j = 0; j < kPiecesPerWave; ++j) {
+      const int r = (64 * (wave + kMlaWaves * j) + lane) / kChunksPerRow;
+      const int e = tile * kMlaTile + r;
+      rid[j] = sh.rowid[e < nvalid ? e : 0];   // rows past the end re-read the split's first row (masked)
     }
-#pragma unroll
-    for (int q = 0; q < kCopies - 1; ++q)
-      st[q] = *reinterpret_cast<const i32x4*>(kvbase + rid[q] * kRowBytes + cp_col[q]);
-    if (five) st[kCopies - 1] = *reinterpret_cast<const i32x4*>(kvbase + rid[kCopies - 1] * kRowBytes + cp_col[kCopies - 1]);
   };
-  auto store_tile = [&](int tile, const i32x4 (&st)[kCopies]) {
-    if (tile >= n_tiles) return;
-    uint8_t* dst = sh.kv[tile % kRing] + 16 * lane;
+  // copies j0 .. j1-1 of this wave for `tile`
+  auto issue_pieces = [&](int tile, const int (&rid)[kPiecesPerWave], int j0, int j1) {
+    const uint32_t dst = lds_offset(sh.kv[tile % kRing]);
 #pragma unroll
-    for (int q = 0; q < kCopies - 1; ++q)
-      *reinterpret_cast<i32x4*>(dst + 1024 * (wave + kMlaWaves * q)) = st[q];
-    if (five) *reinterpret_cast<i32x4*>(dst + 1024 * (wave + kMlaWaves * (kCopies - 1))) = st[kCopies - 1];
+    for (int j = j0; j < j1; ++j) {
+      const int chunk = 64 * (wave + kMlaWaves * j) + lane;
+      const int r = chunk / kChunksPerRow;
+      const int col = ((chunk - r * kChunksPerRow) ^ swz(r)) * 16;
+      lds_dma16(kvbase + (int64_t)rid[j] * kRowBytes + col, dst + 1024 * (wave + kMlaWaves * j));
+    }
+  };
+  auto issue_tile = [&](int tile) {
+    int rid[kPiecesPerWave];
+    fetch_rows(tile, rid);
+    issue_pieces(tile, rid, 0, kPiecesPerWave);
   };
 
   // Consume q here: the compiler then knows its loads have completed, and it
   // places no vector-memory waits inside the tile loop, where they would also
   // drain the (to it invisible) tile copies in flight.
 #pragma unroll
-  for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" :: "v"(qf[ks]));
+  for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" : "+a"(qf[ks]));
 
-
-  f32x4 acc_o[4][4];   // O[heads 16mt + 4g + i][value column 64*wave + 16nt + c]
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc_o[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY;   // running max (log2 units) of head 16*ht + c
-  float l_part = 0.f;        // this lane's share of the softmax denominator
-
-  // score operand: rows c and 16 + c share a swizzle; this wave's half of the row
+  // score operand (A): lane (c, g) reads row c (and 16 + c) of the tile, 16-byte
+  // chunk 4 ks + g of the row. With ks = 2a + u the swizzled position is
+  // 8a + ((4u + g) ^ swz(c)): a per-lane base plus an immediate.
   const int sw_c = swz(c);
-  const int a_row = c * kRowBytes;
-  const int kchunk0 = kh * (kMlaDqk / 2 / 8);        // first 16-byte chunk of the half (36)
-  // value reads: slot jj < 4 -> row 4g + jj, slot jj >= 4 -> row 16 + 4g + jj - 4
-  int v_row[8], v_sw[8];
+  const int a_off0 = c * kRowBytes + (((g) ^ sw_c) << 4);
+  const int a_off1 = c * kRowBytes + (((4 + g) ^ sw_c) << 4);
+  // value operand (B): for rows 16h + 4g + (c >> 2) and value columns
+  // 16nt + 4(c & 3) .. +3; with nt = 4a + u the chunk is 8a + ((2u + ((c & 3) >> 1)) ^ swz(row))
+  int v_off[2][4];
 #pragma unroll
-  for (int jj = 0; jj < 8; ++jj) {
-    const int r = (jj < 4) ? 4 * g + jj : 16 + 4 * g + (jj - 4);
-    v_row[jj] = r * kRowBytes + 2 * (c & 7);
-    v_sw[jj] = swz(r);
+  for (int h = 0; h < 2; ++h) {
+    const int r = 16 * h + 4 * g + (c >> 2);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      v_off[h][u] = r * kRowBytes + (((2 * u + ((c & 3) >> 1)) ^ swz(r)) << 4) + ((c & 1) << 3);
   }
 
-  // ---- helpers of the pipelined loop ----
-  // partial scores of `tile` over this wave's half of the contraction
-  auto scores = [&](int tile, f32x4& own0, f32x4& own1) {
-    const uint8_t* kvt = sh.kv[tile % kRing];
-    f32x4 sa0 = {0.f, 0.f, 0.f, 0.f}, sa1 = sa0, sb0 = sa0, sb1 = sa0;
+  f32x4 acc_o[kVTiles];   // O[head 4g + i][value column 16 nt + c] (PV accumulator layout)
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-      const int o = ((kchunk0 + 4 * ks + g) ^ sw_c) << 4;
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kvt + a_row + o);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kvt + a_row + 16 * kRowBytes + o);
-      if (ks & 1) {
-        sb0 = mfma_bf16(a0, qf[ks], sb0);
-        sb1 = mfma_bf16(a1, qf[ks], sb1);
-      } else {
-        sa0 = mfma_bf16(a0, qf[ks], sa0);
-        sa1 = mfma_bf16(a1, qf[ks], sa1);
+  for (int nt = 0; nt < kVTiles; ++nt) acc_o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY;   // running max (log2 units) of head c
+  float l_part = 0.f;        // this lane's share of head c's softmax denominator
+
+  // S^T of `tile`: s0 rows 4g+i, s1 rows 16+4g+i, head c
+  auto scores = [&](int tile, f32x4& s0, f32x4& s1) {
+    const uint8_t* kvt = sh.kv[tile % kRing];
+    // K operands in batches of three K-steps; batch n + 1 is read before the
+    // MFMAs of batch n
+    constexpr int kB = 3;
+    bf16x8 kop[2][kB][2];
+    auto read_batch = [&](int ks0, bf16x8 (&dst)[kB][2]) {
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int ks = ks0 + u;
+        const int off = ((ks & 1) ? a_off1 : a_off0) + 128 * (ks >> 1);
+        dst[u][0] = *reinterpret_cast<const bf16x8*>(kvt + off);
+        dst[u][1] = *reinterpret_cast<const bf16x8*>(kvt + off + 16 * kRowBytes);
+      }
+    };
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+    read_batch(0, kop[0]);
+#pragma unroll
+    for (int ks0 = 0; ks0 < kKSteps; ks0 += kB) {
+      const int cb = (ks0 / kB) & 1;
+      if (ks0 + kB < kKSteps) read_batch(ks0 + kB, kop[cb ^ 1]);
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        a0 = mfma_bf16(kop[cb][u][0], qf[ks0 + u], a0);
+        a1 = mfma_bf16(kop[cb][u][1], qf[ks0 + u], a1);
       }
     }
-    own0 = sa0 + sb0;
-    own1 = sa1 + sb1;
-    if (kh == 1) {
-      sh.sx[ht][0][lane] = own0;
-      sh.sx[ht][1][lane] = own1;
-    }
-  };
-  // O[64 heads x value columns 64w..64w+63] += P(tile) . V(tile), after the rescale
-  auto pv = [&](int tile) {
-    const int par = tile & 1;
-    const uint8_t* kvt = sh.kv[tile % kRing];
-    if (sh.flag[par]) {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const f32x4 a4 = *reinterpret_cast<const f32x4*>(sh.alpha[par] + 16 * mt + 4 * g);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc_o[mt][nt] *= a4;
-      }
-    }
-    bf16x8 pa[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const uint16_t* pr = sh.pbuf[par] + (16 * mt + c) * kPRow;
-      const u16x4 lo = *reinterpret_cast<const u16x4*>(pr + 4 * g);
-      const u16x4 hi = *reinterpret_cast<const u16x4*>(pr + 16 + 4 * g);
-      const u16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      pa[mt] = __builtin_bit_cast(bf16x8, v);
-    }
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int col = 8 * wave + 2 * nt + (c >> 3);    // 16-byte chunk of value column 64w + 16nt + c
-      u16x8 v;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj)
-        v[jj] = *reinterpret_cast<const uint16_t*>(kvt + v_row[jj] + ((col ^ v_sw[jj]) << 4));
-      const bf16x8 vb = __builtin_bit_cast(bf16x8, v);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) acc_o[mt][nt] = mfma_bf16(pa[mt], vb, acc_o[mt][nt]);
-    }
+    s0 = a0;
+    s1 = a1;
   };
 
-  // Software pipeline, one tile deep: iteration j overlaps the softmax of tile j
-  // (VALU, first-half waves) with P.V of tile j - 1 (MFMA, all waves), stores
-  // tile j + 1 (fetched one iteration earlier) into the slot of tile j - 2 and
-  // fetches tile j + 2; after barrier C it computes the scores of tile j + 1,
-  // and barrier B makes the score halves visible. P, the rescale factors and
-  // the rescale flag are double-buffered by tile parity.
-  i32x4 st[kCopies];
-  f32x4 own0 = {0.f, 0.f, 0.f, 0.f}, own1 = own0;
+  // ---- tile loop ----
+  // Iteration j: wait for tile j + 1, barrier (every wave is done with tile
+  // j - 1, whose slot takes tile j + 3), scores of tile j + 1, softmax and
+  // P.V of tile j, with the copies of tile j + 3 spread over the iteration.
+  // Tiles past the end are copied too (their rows all re-read the split's
+  // first row, a few cache lines) and never used: the loop has no branches
+  // around copies, waits or MFMAs, and every wait is the same.
+  f32x4 cur0 = {0.f, 0.f, 0.f, 0.f}, cur1 = cur0;
   if (n_tiles > 0) {
-    load_tile(0, st);
-    store_tile(0, st);
-    load_tile(1, st);
-    __syncthreads();                                     // tile 0 visible
-    scores(0, own0, own1);
-    __syncthreads();                                     // barrier B of tile 0
+    issue_tile(0);
+    issue_tile(1);
+    issue_tile(2);
+    wait_vmcnt<2 * kPiecesPerWave>();
+    __syncthreads();
+    scores(0, cur0, cur1);
   }
-  // st holds tile + 1 (in flight)
-  auto step = [&](int tile, i32x4 (&X)[kCopies]) {
-    const int par = tile & 1;
-    if (kh == 0) {
-      const f32x4 sc0 = own0 + sh.sx[ht][0][lane];
-      const f32x4 sc1 = own1 + sh.sx[ht][1][lane];
-      // lane (c, g) holds head c, rows 4g+i (sc0) and 16+4g+i (sc1)
-      const int rowbase = tile * kMlaTile;
-      float sv[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sv[i] = sc0[i] * scale_log2;
-        sv[4 + i] = sc1[i] * scale_log2;
-      }
-      if (rowbase + kMlaTile > nvalid) {                 // only the last tile has padding rows
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sv[i] = (rowbase + 4 * g + i < nvalid) ? sv[i] : -INFINITY;
-          sv[4 + i] = (rowbase + 16 + 4 * g + i < nvalid) ? sv[4 + i] : -INFINITY;
-        }
-      }
-      float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                       fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-      mx = max_over_groups(mx);
-      float alpha = 1.f;
-      if (mx > m_ref + kRescaleThreshold) {
-        alpha = __builtin_amdgcn_exp2f(m_ref - mx);
-        m_ref = mx;
-        l_part *= alpha;
-      }
-      if (__ballot(alpha != 1.f) != 0ull && lane == 0) sh.flag[par] = 1;
-      float pr[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pr[i] = __builtin_amdgcn_exp2f(sv[i] - m_ref);
-        l_part += pr[i];
-      }
-      bf16x2 pb[4];                                      // round to nearest even (v_cvt_pk_bf16_f32)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pb[i] = __builtin_convertvector(f32x2{pr[2 * i], pr[2 * i + 1]}, bf16x2);
-      uint16_t* prow = sh.pbuf[par] + (16 * ht + c) * kPRow;
-      *reinterpret_cast<bf16x2*>(prow + 4 * g) = pb[0];
-      *reinterpret_cast<bf16x2*>(prow + 4 * g + 2) = pb[1];
-      *reinterpret_cast<bf16x2*>(prow + 16 + 4 * g) = pb[2];
-      *reinterpret_cast<bf16x2*>(prow + 16 + 4 * g + 2) = pb[3];
-      if (g == 0) sh.alpha[par][16 * ht + c] = alpha;
-    }
-    if (tile > 0) pv(tile - 1);
-    store_tile(tile + 1, X);                             // slot of tile - 2: free since barrier C of tile - 1
-    load_tile(tile + 2, X);
-    __syncthreads();                                     // barrier C
-    if (tid == 0) sh.flag[par ^ 1] = 0;                  // next used by the softmax of tile + 1
-    if (tile + 1 < n_tiles) {
-      scores(tile + 1, own0, own1);
-      __syncthreads();                                   // barrier B of tile + 1
-    }
-  };
-  for (int tile = 0; tile < n_tiles; ++tile) step(tile, st);
-  if (n_tiles > 0) pv(n_tiles - 1);
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    wait_vmcnt<kPiecesPerWave>();                        // tile + 1 has landed, tile + 2 may be in flight
+    __syncthreads();
+    int rid[kPiecesPerWave];
+    fetch_rows(tile + 3, rid);
+    issue_pieces(tile + 3, rid, 0, 3);
 
-  // ---- finish: denominators, lse, normalized output ----
-  if (kh == 0) {
-    const float l = sum_over_groups(l_part);
-    const int hq = head0 + 16 * ht + c;     // head of this lane in the score layout
-    const float lse_val = (l > 0.f) ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
-    if (g == 0) {
-      sh.lsum[16 * ht + c] = l;
-      if (S == 1) {
-        if (p.lse) p.lse[(int64_t)t * Hm + hq] = lse_val;
-      } else {
-        p.part_lse[((int64_t)t * S + s) * Hm + hq] = lse_val;
-      }
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const f32x4 l4 = *reinterpret_cast<const f32x4*>(sh.lsum + 16 * mt + 4 * g);
+    // softmax of tile: lane (c, g) holds head c, rows 4g+i (cur0) and 16+4g+i (cur1)
+    float sv[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int h = head0 + 16 * mt + 4 * g + i;
-      const float inv = l4[i] > 0.f ? 1.f / l4[i] : 0.f;
-      if (S == 1) {
-        uint16_t* orow = static_cast<uint16_t*>(p.out) + ((int64_t)t * Hm + h) * kMlaDl;
+      sv[i] = cur0[i] * scale_log2;
+      sv[4 + i] = cur1[i] * scale_log2;
+    }
+    const int rows_left = nvalid - tile * kMlaTile;      // padding rows (last tile only) -> -inf
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          orow[64 * wave + 16 * nt + c] = f32_to_bf16_bits(acc_o[mt][nt][i] * inv);
-      } else {
-        float* orow = p.part_o + (((int64_t)t * S + s) * Hm + h) * kMlaDl;
+    for (int i = 0; i < 4; ++i) {
+      sv[i] = (4 * g + i < rows_left) ? sv[i] : -INFINITY;
+      sv[4 + i] = (16 + 4 * g + i < rows_left) ? sv[4 + i] : -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    mx = max_over_groups(mx);
+    float alpha = 1.f;
+    if (mx > m_ref + kRescaleThreshold) {
+      alpha = __builtin_amdgcn_exp2f(m_ref - mx);
+      m_ref = mx;
+      l_part *= alpha;
+    }
+    float pr[8];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) orow[64 * wave + 16 * nt + c] = acc_o[mt][nt][i] * inv;
+    for (int i = 0; i < 8; ++i) {
+      pr[i] = __builtin_amdgcn_exp2f(sv[i] - m_ref);
+      l_part += pr[i];
+    }
+    bf16x8 pa;                                           // round to nearest even (v_cvt_pk_bf16_f32)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16x2 two = __builtin_convertvector(f32x2{pr[2 * i], pr[2 * i + 1]}, bf16x2);
+      pa[2 * i] = two[0];
+      pa[2 * i + 1] = two[1];
+    }
+    if (__ballot(alpha != 1.f) != 0ull) {               // rare: rescale O rows (heads 4g + i)
+      float a4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a4[i] = __shfl(alpha, 4 * g + i, kWave);
+#pragma unroll
+      for (int nt = 0; nt < kVTiles; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc_o[nt][i] *= a4[i];
+    }
+
+    issue_pieces(tile + 3, rid, 3, 6);
+    // scores of tile + 1 (independent of the P.V below, so the two MFMA
+    // streams and their LDS reads interleave; the last iteration scores a
+    // stale slot and discards the result)
+    f32x4 nxt0, nxt1;
+    scores(tile + 1, nxt0, nxt1);
+    issue_pieces(tile + 3, rid, 6, kPiecesPerWave);
+
+    // O += P . V(tile)
+    const uint8_t* kvt = sh.kv[tile % kRing];
+    // value operands in batches of eight column tiles; batch n + 1 is read
+    // before the MFMAs of batch n
+    i16x4 vlo[2][8], vhi[2][8];
+    auto read_batch = [&](int n8, i16x4 (&lo)[8], i16x4 (&hi)[8]) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int nt = n8 + u;
+        const int imm = 128 * (nt >> 2);
+        lo[u] = lds_read_tr16(kvt + v_off[0][nt & 3] + imm);
+        hi[u] = lds_read_tr16(kvt + v_off[1][nt & 3] + imm);
       }
+    };
+    read_batch(0, vlo[0], vhi[0]);
+#pragma unroll
+    for (int n8 = 0; n8 < kVTiles; n8 += 8) {
+      const int cb = (n8 >> 3) & 1;
+      if (n8 + 8 < kVTiles) read_batch(n8 + 8, vlo[cb ^ 1], vhi[cb ^ 1]);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const i16x8 v8 = __builtin_shufflevector(vlo[cb][u], vhi[cb][u], 0, 1, 2, 3, 4, 5, 6, 7);
+        acc_o[n8 + u] = mfma_bf16(pa, __builtin_bit_cast(bf16x8, v8), acc_o[n8 + u]);
+      }
+    }
+    cur0 = nxt0;
+    cur1 = nxt1;
+  }
+  wait_vmcnt<0>();                                       // no copy into LDS outlives the loop
+
+  // ---- finish: denominators, lse, normalized output ----
+  const float l = sum_over_groups(l_part);               // head c
+  if (g == 0) {
+    const float lse_val = (l > 0.f) ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
+    if (S == 1) {
+      if (p.lse) p.lse[(int64_t)t * Hm + head0 + c] = lse_val;
+    } else {
+      p.part_lse[((int64_t)t * S + s) * Hm + head0 + c] = lse_val;
+    }
+  }
+  float inv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float li = __shfl(l, 4 * g + i, kWave);        // head 4g + i
+    inv[i] = li > 0.f ? 1.f / li : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = head0 + 4 * g + i;
+    if (S == 1) {
+      uint16_t* orow = static_cast<uint16_t*>(p.out) + ((int64_t)t * Hm + h) * kMlaDl;
+#pragma unroll
+      for (int nt = 0; nt < kVTiles; ++nt) orow[16 * nt + c] = f32_to_bf16_bits(acc_o[nt][i] * inv[i]);
+    } else {
+      float* orow = p.part_o + (((int64_t)t * S + s) * Hm + h) * kMlaDl;
+#pragma unroll
+      for (int nt = 0; nt < kVTiles; ++nt) orow[16 * nt + c] = acc_o[nt][i] * inv[i];
     }
   }
 }
