@@ -14,9 +14,12 @@
 // Rows of up to 32768 scores are read from HBM once: each thread keeps sixteen
 // 16-byte loads in flight (the whole row is requested at once), converts them to
 // keys into LDS and counts the first digit on the way. Longer rows are re-read
-// from global memory (L2) by each pass. Every pass handles 8 consecutive
-// positions per thread; the ordered output pass needs one block-wide scan per
-// 4096 positions.
+// from global memory (L2) by each pass. The histogram passes handle 8
+// consecutive positions per thread per step; keys sharing the first digit with
+// the k-th largest are appended (wave-aggregated) to a candidate list for the
+// last digit. The ordered output gives each thread one contiguous run of
+// positions: count winners in the run, one block-wide scan, write the run's
+// winners in order.
 #include "device_common.h"
 #include "dsa_internal.h"
 
@@ -30,6 +33,8 @@ constexpr int kTkBins = 4096;
 constexpr int kTkLoadUnroll = 16;          // float4 loads in flight per thread
 constexpr int kTkPer = 8;                  // consecutive positions per thread per pass step
 constexpr int kTkCand = 4032;              // keys sharing the top 12 bits kept for the last level
+constexpr int kTkRun = kTkCache / kTkThreads;   // 64 positions per thread in the output pass (cached rows)
+static_assert(kTkRun == 64, "the output pass handles one 64-position mask per cached run");
 
 struct TopkShared {
   uint32_t hist[kTkBins];
@@ -41,12 +46,20 @@ struct TopkShared {
   uint32_t sel_above;
 };
 
+// LDS word of position p. Each run of 64 positions (one thread's run in the
+// output pass) keeps its sixteen 16-byte blocks, block j stored at j ^ (run % 16),
+// so that consecutive threads reading their runs block by block, and
+// consecutive threads reading consecutive blocks, hit distinct banks.
+__device__ __forceinline__ int kslot(int p) {
+  return (p & ~63) | ((((p >> 2) & 15) ^ ((p >> 6) & 15)) << 2) | (p & 3);
+}
+
 // Keys of positions [i, i + 8) (i a multiple of 8); positions >= n give 0.
 __device__ __forceinline__ void load8(const float* __restrict__ row, const TopkShared& sh, bool cached,
                                       int n, int i, uint32_t (&u)[kTkPer]) {
   if (cached) {
-    const i32x4 a = *reinterpret_cast<const i32x4*>(sh.keys + i);
-    const i32x4 b = *reinterpret_cast<const i32x4*>(sh.keys + i + 4);
+    const i32x4 a = *reinterpret_cast<const i32x4*>(sh.keys + kslot(i));
+    const i32x4 b = *reinterpret_cast<const i32x4*>(sh.keys + kslot(i + 4));
 #pragma unroll
     for (int e = 0; e < 4; ++e) { u[e] = (uint32_t)a[e]; u[4 + e] = (uint32_t)b[e]; }
   } else {
@@ -157,13 +170,13 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
           atomicAdd(&sh.hist[kk[e] >> 20], 1u);
         }
         if (cached)
-          *reinterpret_cast<i32x4*>(sh.keys + 4 * i4) = i32x4{(int)kk[0], (int)kk[1], (int)kk[2], (int)kk[3]};
+          *reinterpret_cast<i32x4*>(sh.keys + kslot(4 * i4)) = i32x4{(int)kk[0], (int)kk[1], (int)kk[2], (int)kk[3]};
       }
     }
   }
   for (int i = 4 * n4 + tid; i < n; i += kTkThreads) {
     const uint32_t kk = ordered_key(row[i]);
-    if (cached) sh.keys[i] = kk;
+    if (cached) sh.keys[kslot(i)] = kk;
     atomicAdd(&sh.hist[kk >> 20], 1u);
   }
   __syncthreads();
@@ -183,12 +196,24 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
   for (int i = kTkPer * tid; i < n; i += kTkPer * kTkThreads) {
     uint32_t u[kTkPer];
     load8(row, sh, cached, n, i, u);
+    // matches are rare: each round handles one match per lane, so a wave issues
+    // as many LDS atomics as its busiest lane has matches (not one per element)
+    uint32_t mm = 0;
 #pragma unroll
-    for (int e = 0; e < kTkPer; ++e)
-      if (i + e < n && (u[e] >> 20) == prefix) {
-        atomicAdd(&sh.hist[(u[e] >> 8) & 0xfffu], 1u);
-        if (keep) sh.cand[atomicAdd(&sh.n_cand, 1u)] = u[e];
+    for (int e = 0; e < kTkPer; ++e) mm |= ((i + e < n && (u[e] >> 20) == prefix) ? 1u : 0u) << e;
+    while (__ballot(mm != 0u)) {
+      const bool m = mm != 0u;
+      uint32_t x = 0;
+      if (m) {
+        const int e = __builtin_ctz(mm);
+        mm &= mm - 1u;
+        x = u[0];
+#pragma unroll
+        for (int q = 1; q < kTkPer; ++q) x = (e == q) ? u[q] : x;
+        atomicAdd(&sh.hist[(x >> 8) & 0xfffu], 1u);
       }
+      if (keep && m) sh.cand[atomicAdd(&sh.n_cand, 1u)] = x;   // (the compiler merges a wave's increments)
+    }
   }
   __syncthreads();
   select_bin(sh, kTkBins, need, 1, &bin, &above);
@@ -219,53 +244,75 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
   need -= above;  // how many keys equal to thr are among the winners (>= 1)
 
   // ---- ordered output ----
-  // position of a winner = (#keys > thr before it) + min(#keys == thr before it, need)
-  uint32_t base_gt = 0, base_eq = 0;
-  int it = 1;
-  for (int i0 = 0; i0 < n; i0 += kTkPer * kTkThreads, ++it) {
-    const int i = i0 + kTkPer * tid;
-    uint32_t u[kTkPer];
-    if (i < n) {
-      load8(row, sh, cached, n, i, u);
+  // A winner at position p goes to slot #winners before p = (#keys > thr before
+  // p) + min(#keys == thr before p, need). Thread tid owns a run of
+  // consecutive positions, handled 64 at a time as bit masks: count its winners,
+  // one block-wide scan, then write them in order.
+  const int run_len = cached ? kTkRun : ((n + kTkThreads - 1) / kTkThreads + 63) & ~63;
+  const int run0 = run_len * tid;
+  // masks of the keys > thr and == thr among positions [p0, p0 + 64)
+  auto masks64 = [&](int p0, uint64_t* gtm, uint64_t* eqm) {
+    uint32_t key[64];
+    if (cached) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const i32x4 a = *reinterpret_cast<const i32x4*>(sh.keys + kslot(p0 + 4 * j));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) key[4 * j + e] = (uint32_t)a[e];
+      }
     } else {
 #pragma unroll
-      for (int e = 0; e < kTkPer; ++e) u[e] = 0u;
-    }
-    uint32_t cgt = 0, ceq = 0;
+      for (int j = 0; j < 8; ++j) {
+        uint32_t u[kTkPer];
+        load8(row, sh, false, n, p0 + 8 * j, u);
 #pragma unroll
-    for (int e = 0; e < kTkPer; ++e) {
-      const bool valid = i + e < n;
-      cgt += (valid && u[e] > thr) ? 1u : 0u;
-      ceq += (valid && u[e] == thr) ? 1u : 0u;
-    }
-    // counts per thread are <= 8 and per block <= 4096: pack (gt, eq) in one word
-    uint32_t total;
-    const uint32_t packed = (cgt << 16) | ceq;
-    const uint32_t excl = block_scan(sh, packed, it & 1, &total) - packed;
-    // winner e goes to (#gt before it) + min(#eq before it, need); the same
-    // formula covers both kinds because a taken tie has #eq before it < need
-    uint32_t gt_before = base_gt + (excl >> 16);
-    uint32_t eq_before = base_eq + (excl & 0xffffu);
-    if (packed) {
-      uint32_t pos[kTkPer];
-      bool take[kTkPer];
-#pragma unroll
-      for (int e = 0; e < kTkPer; ++e) {
-        const bool valid = i + e < n;
-        const bool isgt = valid && u[e] > thr;
-        const bool iseq = valid && u[e] == thr;
-        take[e] = isgt || (iseq && eq_before < need);
-        pos[e] = gt_before + (eq_before < need ? eq_before : need);
-        gt_before += isgt ? 1u : 0u;
-        eq_before += iseq ? 1u : 0u;
+        for (int e = 0; e < kTkPer; ++e) key[8 * j + e] = u[e];
       }
-#pragma unroll
-      for (int e = 0; e < kTkPer; ++e)
-        if (take[e] && pos[e] < (uint32_t)k) out[pos[e]] = i + e;
     }
-    base_gt += total >> 16;
-    base_eq += total & 0xffffu;
-    if (base_gt + (base_eq < need ? base_eq : need) >= (uint32_t)k) break;
+    uint32_t g0 = 0, g1 = 0, q0 = 0, q1 = 0;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      g0 |= (key[e] > thr ? 1u : 0u) << e;
+      q0 |= (key[e] == thr ? 1u : 0u) << e;
+      g1 |= (key[32 + e] > thr ? 1u : 0u) << e;
+      q1 |= (key[32 + e] == thr ? 1u : 0u) << e;
+    }
+    const int nv = n - p0;                                  // valid positions in the block
+    const uint64_t vmask = nv >= 64 ? ~0ull : (nv <= 0 ? 0ull : ((1ull << nv) - 1ull));
+    *gtm = (((uint64_t)g1 << 32) | g0) & vmask;
+    *eqm = (((uint64_t)q1 << 32) | q0) & vmask;
+  };
+  uint32_t cgt = 0, ceq = 0;
+  for (int p0 = run0; p0 < run0 + run_len && p0 < n; p0 += 64) {
+    uint64_t gtm, eqm;
+    masks64(p0, &gtm, &eqm);
+    cgt += (uint32_t)__builtin_popcountll(gtm);
+    ceq += (uint32_t)__builtin_popcountll(eqm);
+  }
+  uint32_t total_gt, total_eq;
+  const uint32_t gt_incl = block_scan(sh, cgt, 1, &total_gt);
+  const uint32_t eq_incl = block_scan(sh, ceq, 0, &total_eq);
+  uint32_t eq_before = eq_incl - ceq;
+  uint32_t slot = (gt_incl - cgt) + (eq_before < need ? eq_before : need);
+  if (cgt + ceq) {
+    for (int p0 = run0; p0 < run0 + run_len && p0 < n; p0 += 64) {
+      uint64_t gtm, eqm;
+      masks64(p0, &gtm, &eqm);
+      // the first (need - eq_before) ties of the block are winners
+      uint64_t win = gtm;
+      for (uint32_t r = eq_before; r < need && eqm; ++r) {
+        const uint64_t low = eqm & (0ull - eqm);
+        win |= low;
+        eqm ^= low;
+      }
+      eq_before += (uint32_t)__builtin_popcountll(eqm) + (uint32_t)__builtin_popcountll(win & ~gtm);
+      while (win) {
+        const int e = __builtin_ctzll(win);
+        if (slot < (uint32_t)k) out[slot] = p0 + e;
+        ++slot;
+        win &= win - 1ull;
+      }
+    }
   }
 }
 
