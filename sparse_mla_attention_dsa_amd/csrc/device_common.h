@@ -84,4 +84,21 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
   return v;
 }
 
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>(p);   // LDS aperture: low 32 bits are the offset
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at M0 + 16 l (M0 = the wave-uniform destination). Completion is counted by
+// vmcnt like any other vector load.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(gsrc), "s"(lds_addr) : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
 }  // namespace dsa

@@ -125,6 +125,194 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_fp8_kernel(IndexerPara
   }
 }
 
+// Decode rows (one query row per request): a streaming variant. The keys of
+// all rows are cut into groups of 16 (row t has ceil(visible_t / 16) groups);
+// every wave of a fixed grid takes an equal contiguous share of the flattened
+// group list, whatever the row lengths, and walks it in batches of up to four
+// groups inside one page. The batch list of a wave is built once (lane j holds
+// batch j's row, first group, count, page and row length; all page lookups in
+// one vector load), then the wave streams: the loads of batch j + 1 are issued
+// before the MFMAs of batch j. q and the head weights are reloaded when the
+// row changes (once or twice per wave). Every wave is independent: no barrier
+// after the row prefix sums.
+constexpr int kStreamThreads = 256;
+constexpr int kStreamWaves = kStreamThreads / kWave;
+constexpr int kStreamMaxRows = 1024;
+constexpr int kStreamBatch = 4;                                  // groups per batch
+
+struct StreamBatch {
+  int t, gi, cnt;
+};
+
+__global__ __launch_bounds__(kStreamThreads) void indexer_fp8_stream_kernel(IndexerParams p) {
+  __shared__ int pre[kStreamMaxRows + 1];                        // group prefix over rows
+  __shared__ int wsum[kStreamWaves];
+  const BatchView& bv = p.batch;
+  const int T = bv.num_rows;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(wave_id());
+  const int g = lane >> 4, c = lane & 15;
+  const int P = bv.page_size;
+  const int gpp = P / 16;                                        // groups per page
+  int cap = bv.max_pages_per_seq * P;
+  if (cap > bv.max_seq_len_k) cap = bv.max_seq_len_k;
+  if ((int64_t)cap > p.stride) cap = (int)p.stride;
+
+  // ---- groups per row and their prefix sums ----
+  int carry = 0;
+  for (int base = 0; base < T; base += kStreamThreads) {
+    const int t = base + tid;
+    const int vis = t < T ? visible_keys(bv.seq_lens_k[t], 1, 0, cap) : 0;
+    const int cnt = (vis + 15) >> 4;
+    const int incl = (int)wave_inclusive_scan((uint32_t)cnt);
+    if (lane == kWave - 1) wsum[wave] = incl;
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kStreamWaves; ++w) {
+      const int v = wsum[w];
+      before += (w < wave) ? v : 0;
+      tot += v;
+    }
+    if (t < T) pre[t + 1] = carry + before + incl;
+    carry += tot;
+    __syncthreads();
+  }
+  if (tid == 0) pre[0] = 0;
+  __syncthreads();
+
+  const int N = pre[T];
+  const int W = gridDim.x * kStreamWaves;
+  const int wg = blockIdx.x * kStreamWaves + wave;
+  int a = (int)((int64_t)N * wg / W);
+  const int a_end = (int)((int64_t)N * (wg + 1) / W);
+  if (a >= a_end) return;
+  // row of group a: the largest t with pre[t] <= a (rows without groups are passed over)
+  int t = 0;
+  {
+    int lo = 0, hi = T - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= a) lo = mid; else hi = mid - 1;
+    }
+    t = lo;
+  }
+  t = __builtin_amdgcn_readfirstlane(t);
+  int gi = a - pre[t];
+  gi = __builtin_amdgcn_readfirstlane(gi);
+
+  const int64_t scale_off = (int64_t)P * kIdxDim;
+  const uint8_t* cache = p.cache;
+  while (a < a_end) {
+    // ---- batch list (up to 64 batches): lane j holds batch j ----
+    int bt_t = 0, bt_gi = 0, bt_cnt = 0, nb = 0;
+    while (a < a_end && nb < kWave) {
+      int n_t = pre[t + 1] - pre[t];
+      while (gi >= n_t) {                                        // next row with groups
+        ++t;
+        gi = 0;
+        n_t = pre[t + 1] - pre[t];
+      }
+      int gend = (gi / gpp + 1) * gpp;
+      gend = min(gend, gi + kStreamBatch);
+      gend = min(gend, n_t);
+      gend = min(gend, gi + (a_end - a));
+      if (lane == nb) { bt_t = t; bt_gi = gi; bt_cnt = gend - gi; }
+      a += gend - gi;
+      gi = gend;
+      ++nb;
+    }
+    // pages and row lengths of every batch in one go
+    int bt_page = -1, bt_vis = 0;
+    if (lane < nb) {
+      const int pi = bt_gi / gpp;
+      bt_page = bv.block_table[(int64_t)bt_t * bv.max_pages_per_seq + pi];
+      bt_vis = visible_keys(bv.seq_lens_k[bt_t], 1, 0, cap);
+    }
+
+    auto batch_of = [&](int j, int* bt, int* bg, int* bc, int* bp, int* bvv) {
+      *bt = __builtin_amdgcn_readlane(bt_t, j);
+      *bg = __builtin_amdgcn_readlane(bt_gi, j);
+      *bc = __builtin_amdgcn_readlane(bt_cnt, j);
+      *bp = __builtin_amdgcn_readlane(bt_page, j);
+      *bvv = __builtin_amdgcn_readlane(bt_vis, j);
+    };
+    // key operands (lane (c, g): key 16u + c of the batch, bytes [32g, 32g + 32)) and scales
+    auto load_batch = [&](int bg, int bc, int bp, i32x8 (&kb)[kStreamBatch], float (&sg)[kStreamBatch]) {
+      const bool okp = bp >= 0 && bp < bv.num_pages;
+      const uint8_t* pg = cache + (int64_t)(okp ? bp : 0) * p.page_bytes;
+#pragma unroll
+      for (int u = 0; u < kStreamBatch; ++u) {
+        const int uu = u < bc ? u : 0;                           // past the batch: re-read group 0
+        const int slot = (16 * (bg + uu)) % P + c;
+        kb[u] = *reinterpret_cast<const i32x8*>(pg + (int64_t)slot * kIdxDim + 32 * g);
+        sg[u] = *reinterpret_cast<const float*>(pg + scale_off + 4 * slot);
+      }
+    };
+
+    i32x8 qa[4];
+    float wv[16];
+    int q_row = -1;
+    auto load_row = [&](int rt) {
+      const uint8_t* qr = static_cast<const uint8_t*>(p.q) + (int64_t)rt * (kIdxHeads * kIdxDim);
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        qa[m] = *reinterpret_cast<const i32x8*>(qr + (16 * m + c) * kIdxDim + 32 * g);
+      const float* wrow = p.w + (int64_t)rt * kIdxHeads;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const f32x4 w4 = *reinterpret_cast<const f32x4*>(wrow + 16 * m + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wv[4 * m + i] = w4[i];
+      }
+      q_row = rt;
+    };
+
+    // one batch in flight ahead of the one being computed
+    int ct, cg, cc, cp, cv;
+    batch_of(0, &ct, &cg, &cc, &cp, &cv);
+    i32x8 k0[kStreamBatch];
+    float s0[kStreamBatch];
+    load_batch(cg, cc, cp, k0, s0);
+    load_row(ct);
+    for (int j = 0; j < nb; ++j) {
+      int nt_ = 0, ng = 0, nc = 0, np = -1, nv = 0;
+      i32x8 k1[kStreamBatch];
+      float s1[kStreamBatch];
+      const bool more = j + 1 < nb;
+      if (more) {
+        batch_of(j + 1, &nt_, &ng, &nc, &np, &nv);
+        load_batch(ng, nc, np, k1, s1);
+      }
+      if (ct != q_row) load_row(ct);
+      // ---- logits of batch j ----
+      const bool okp = cp >= 0 && cp < bv.num_pages;
+      float* out = p.logits + (int64_t)ct * p.stride;
+#pragma unroll
+      for (int u = 0; u < kStreamBatch; ++u) {
+        if (u >= cc) break;
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        float part = 0.f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const f32x4 acc = mfma_fp8_16x16x128(qa[m], k0[u], zero);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) part = fmaf(wv[4 * m + i], fmaxf(acc[i], 0.f), part);
+        }
+        part += shfl_xor_f(part, 16);
+        part += shfl_xor_f(part, 32);
+        const int s = 16 * (cg + u) + c;
+        if (g == 0 && s < cv) out[s] = okp ? part * s0[u] : -INFINITY;
+      }
+      if (!more) break;
+      ct = nt_; cg = ng; cc = nc; cp = np; cv = nv;
+#pragma unroll
+      for (int u = 0; u < kStreamBatch; ++u) { k0[u] = k1[u]; s0[u] = s1[u]; }
+    }
+  }
+}
+
 // fp32 keys (H <= 64, D <= 128): one thread per key, q of the row staged in LDS.
 constexpr int kF32Block = 256;
 
@@ -168,6 +356,15 @@ __global__ __launch_bounds__(kF32Block) void indexer_f32_kernel(IndexerParams p)
 hipError_t launch_indexer_fp8(const IndexerParams& p, hipStream_t s) {
   const int chunks = (p.batch.max_seq_len_k + kIdxChunk - 1) / kIdxChunk;
   if (p.batch.num_rows == 0 || chunks == 0) return hipSuccess;
+  if (p.batch.cu_seqlens_q == nullptr && p.batch.num_rows <= kStreamMaxRows) {
+    // about 32 groups per wave, at most three work-groups per CU (one round)
+    const int64_t groups = (int64_t)p.batch.num_rows * ((p.batch.max_seq_len_k + 15) / 16);
+    int64_t wgs = (groups / 32 + kStreamWaves - 1) / kStreamWaves;
+    if (wgs > 768) wgs = 768;
+    if (wgs < 1) wgs = 1;
+    hipLaunchKernelGGL(indexer_fp8_stream_kernel, dim3((unsigned)wgs), dim3(kStreamThreads), 0, s, p);
+    return hipGetLastError();
+  }
   dim3 grid(p.batch.num_rows, chunks);
   hipLaunchKernelGGL(indexer_fp8_kernel, grid, dim3(64 * kIdxWaves), 0, s, p);
   return hipGetLastError();

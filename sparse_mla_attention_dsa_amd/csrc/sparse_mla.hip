@@ -101,23 +101,6 @@ __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, con
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t lds_offset(const void* p) {
-  return (uint32_t)reinterpret_cast<uintptr_t>(p);   // LDS aperture: low 32 bits are the offset
-}
-
-// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
-// at M0 + 16 l (M0 = the wave-uniform destination). Completion is counted by
-// vmcnt like any other vector load.
-__device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(gsrc), "s"(lds_addr) : "memory", "m0");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
-
 // transposing LDS read: lane 4k + m of each 16-lane block names 8 bytes (four
 // bf16) of row k; lane i of the block receives element i % 4 of lane
 // 4 * kk + i / 4's bytes in slot kk, i.e. one column of four rows
