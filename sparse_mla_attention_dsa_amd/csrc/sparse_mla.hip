@@ -252,36 +252,47 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
   float m_ref = -INFINITY;   // running max (log2 units) of head c
   float l_part = 0.f;        // this lane's share of head c's softmax denominator
 
-  // S^T of `tile`: s0 rows 4g+i, s1 rows 16+4g+i, head c
-  auto scores = [&](int tile, f32x4& s0, f32x4& s1) {
-    const uint8_t* kvt = sh.kv[tile % kRing];
-    // K operands in batches of three K-steps; batch n + 1 is read before the
-    // MFMAs of batch n
-    constexpr int kB = 3;
-    bf16x8 kop[2][kB][2];
-    auto read_batch = [&](int ks0, bf16x8 (&dst)[kB][2]) {
+  // Score operands of K-steps 3b .. 3b+2 (rows c and 16 + c of the tile) and
+  // their MFMAs into S^T: s0 rows 4g+i, s1 rows 16+4g+i, head c.
+  constexpr int kKB = 3;                                 // K-steps per batch
+  constexpr int kKBatches = kKSteps / kKB;               // 6
+  auto read_k = [&](const uint8_t* kvt, int b, bf16x8 (&dst)[kKB][2]) {
 #pragma unroll
-      for (int u = 0; u < kB; ++u) {
-        const int ks = ks0 + u;
-        const int off = ((ks & 1) ? a_off1 : a_off0) + 128 * (ks >> 1);
-        dst[u][0] = *reinterpret_cast<const bf16x8*>(kvt + off);
-        dst[u][1] = *reinterpret_cast<const bf16x8*>(kvt + off + 16 * kRowBytes);
-      }
-    };
-    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
-    read_batch(0, kop[0]);
-#pragma unroll
-    for (int ks0 = 0; ks0 < kKSteps; ks0 += kB) {
-      const int cb = (ks0 / kB) & 1;
-      if (ks0 + kB < kKSteps) read_batch(ks0 + kB, kop[cb ^ 1]);
-#pragma unroll
-      for (int u = 0; u < kB; ++u) {
-        a0 = mfma_bf16(kop[cb][u][0], qf[ks0 + u], a0);
-        a1 = mfma_bf16(kop[cb][u][1], qf[ks0 + u], a1);
-      }
+    for (int u = 0; u < kKB; ++u) {
+      const int ks = kKB * b + u;
+      const int off = ((ks & 1) ? a_off1 : a_off0) + 128 * (ks >> 1);
+      dst[u][0] = *reinterpret_cast<const bf16x8*>(kvt + off);
+      dst[u][1] = *reinterpret_cast<const bf16x8*>(kvt + off + 16 * kRowBytes);
     }
-    s0 = a0;
-    s1 = a1;
+  };
+  auto mfma_k = [&](int b, const bf16x8 (&op)[kKB][2], f32x4& s0, f32x4& s1) {
+#pragma unroll
+    for (int u = 0; u < kKB; ++u) {
+      s0 = mfma_bf16(op[u][0], qf[kKB * b + u], s0);
+      s1 = mfma_bf16(op[u][1], qf[kKB * b + u], s1);
+    }
+  };
+  // value operands of column tiles 8n .. 8n+7 (two transposing reads each)
+  constexpr int kVB = 8;
+  auto read_v = [&](const uint8_t* kvt, int n, i16x4 (&lo)[kVB], i16x4 (&hi)[kVB]) {
+#pragma unroll
+    for (int u = 0; u < kVB; ++u) {
+      const int nt = kVB * n + u;
+      const int imm = 128 * (nt >> 2);
+      lo[u] = lds_read_tr16(kvt + v_off[0][nt & 3] + imm);
+      hi[u] = lds_read_tr16(kvt + v_off[1][nt & 3] + imm);
+    }
+  };
+  auto scores = [&](int tile, f32x4& s0, f32x4& s1) {   // (prologue only)
+    const uint8_t* kvt = sh.kv[tile % kRing];
+    s0 = f32x4{0.f, 0.f, 0.f, 0.f};
+    s1 = s0;
+#pragma unroll
+    for (int b = 0; b < kKBatches; ++b) {
+      bf16x8 op[kKB][2];
+      read_k(kvt, b, op);
+      mfma_k(b, op, s0, s1);
+    }
   };
 
   // ---- tile loop ----
@@ -306,6 +317,19 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
     int rid[kPiecesPerWave];
     fetch_rows(tile + 3, rid);
     issue_pieces(tile + 3, rid, 0, 3);
+
+    // The iteration is one software pipeline, fenced so that the compiler
+    // keeps it: operand reads of the next batch are issued before the MFMAs
+    // of the current one, first over the six score batches of tile + 1, then
+    // over the four value batches of tile. The softmax of tile (VALU) runs
+    // while the first score operands are in flight. (The last iteration
+    // scores a stale slot and discards the result.)
+    const uint8_t* kvn = sh.kv[(tile + 1) % kRing];
+    const uint8_t* kvt = sh.kv[tile % kRing];
+    bf16x8 kop[2][kKB][2];
+    i16x4 vlo[2][kVB], vhi[2][kVB];
+    read_k(kvn, 0, kop[0]);
+    __builtin_amdgcn_sched_barrier(0);
 
     // softmax of tile: lane (c, g) holds head c, rows 4g+i (cur0) and 16+4g+i (cur1)
     float sv[8];
@@ -352,38 +376,29 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
         for (int i = 0; i < 4; ++i) acc_o[nt][i] *= a4[i];
     }
 
-    issue_pieces(tile + 3, rid, 3, 6);
-    // scores of tile + 1 (independent of the P.V below, so the two MFMA
-    // streams and their LDS reads interleave; the last iteration scores a
-    // stale slot and discards the result)
-    f32x4 nxt0, nxt1;
-    scores(tile + 1, nxt0, nxt1);
-    issue_pieces(tile + 3, rid, 6, kPiecesPerWave);
-
+    // scores of tile + 1
+    f32x4 nxt0 = {0.f, 0.f, 0.f, 0.f}, nxt1 = nxt0;
+#pragma unroll
+    for (int b = 0; b < kKBatches; ++b) {
+      if (b + 1 < kKBatches) read_k(kvn, b + 1, kop[(b + 1) & 1]);
+      else read_v(kvt, 0, vlo[0], vhi[0]);
+      if (b == 1) issue_pieces(tile + 3, rid, 3, 6);
+      if (b == 3) issue_pieces(tile + 3, rid, 6, kPiecesPerWave);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_k(b, kop[b & 1], nxt0, nxt1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // O += P . V(tile)
-    const uint8_t* kvt = sh.kv[tile % kRing];
-    // value operands in batches of eight column tiles; batch n + 1 is read
-    // before the MFMAs of batch n
-    i16x4 vlo[2][8], vhi[2][8];
-    auto read_batch = [&](int n8, i16x4 (&lo)[8], i16x4 (&hi)[8]) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int nt = n8 + u;
-        const int imm = 128 * (nt >> 2);
-        lo[u] = lds_read_tr16(kvt + v_off[0][nt & 3] + imm);
-        hi[u] = lds_read_tr16(kvt + v_off[1][nt & 3] + imm);
+    for (int n = 0; n < kVTiles / kVB; ++n) {
+      if (n + 1 < kVTiles / kVB) read_v(kvt, n + 1, vlo[(n + 1) & 1], vhi[(n + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < kVB; ++u) {
+        const i16x8 v8 = __builtin_shufflevector(vlo[n & 1][u], vhi[n & 1][u], 0, 1, 2, 3, 4, 5, 6, 7);
+        acc_o[kVB * n + u] = mfma_bf16(pa, __builtin_bit_cast(bf16x8, v8), acc_o[kVB * n + u]);
       }
-    };
-    read_batch(0, vlo[0], vhi[0]);
-#pragma unroll
-    for (int n8 = 0; n8 < kVTiles; n8 += 8) {
-      const int cb = (n8 >> 3) & 1;
-      if (n8 + 8 < kVTiles) read_batch(n8 + 8, vlo[cb ^ 1], vhi[cb ^ 1]);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const i16x8 v8 = __builtin_shufflevector(vlo[cb][u], vhi[cb][u], 0, 1, 2, 3, 4, 5, 6, 7);
-        acc_o[n8 + u] = mfma_bf16(pa, __builtin_bit_cast(bf16x8, v8), acc_o[n8 + u]);
-      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     cur0 = nxt0;
     cur1 = nxt1;
