@@ -34,6 +34,7 @@ constexpr int kTkLoadUnroll = 16;          // float4 loads in flight per thread
 constexpr int kTkPer = 8;                  // consecutive positions per thread per pass step
 constexpr int kTkCand = 4032;              // keys sharing the top 12 bits kept for the last level
 constexpr int kTkRun = kTkCache / kTkThreads;   // 64 positions per thread in the output pass (cached rows)
+constexpr int kTkCandPerWave = kTkCand / kTkWaves; // 504 candidate slots per wave
 static_assert(kTkRun == 64, "the output pass handles one 64-position mask per cached run");
 
 struct TopkShared {
@@ -41,6 +42,7 @@ struct TopkShared {
   alignas(16) uint32_t keys[kTkCache];
   uint32_t cand[kTkCand];
   uint32_t n_cand;
+  uint32_t wave_cand[kTkWaves];
   uint32_t wave_sum[2][kTkWaves];
   uint32_t sel_bin;
   uint32_t sel_above;
@@ -76,6 +78,10 @@ __device__ __forceinline__ void load8(const float* __restrict__ row, const TopkS
 // Inclusive scan of v over the work-group in thread order; returns the
 // inclusive prefix and stores the total in *total. One barrier; `buf` selects
 // the double-buffered wave totals so consecutive calls need no extra barrier.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
 __device__ __forceinline__ uint32_t block_scan(TopkShared& sh, uint32_t v, int buf, uint32_t* total) {
   const int lane = lane_id(), wave = wave_id();
   const uint32_t incl = wave_inclusive_scan(v);
@@ -193,6 +199,11 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
   for (int i = tid; i < kTkBins; i += kTkThreads) sh.hist[i] = 0;
   if (tid == 0) sh.n_cand = 0;
   __syncthreads();
+  // Each wave appends its matches to its own 504 slots of the list (ballot and
+  // lane rank: no returning atomics in the loop); a wave that runs out of
+  // slots makes the last digit take the full pass instead.
+  const int wave = wave_id();
+  uint32_t wcnt = 0;                                   // this wave's matches so far (wave-uniform)
   for (int i = kTkPer * tid; i < n; i += kTkPer * kTkThreads) {
     uint32_t u[kTkPer];
     load8(row, sh, cached, n, i, u);
@@ -212,9 +223,13 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
         for (int q = 1; q < kTkPer; ++q) x = (e == q) ? u[q] : x;
         atomicAdd(&sh.hist[(x >> 8) & 0xfffu], 1u);
       }
-      if (keep && m) sh.cand[atomicAdd(&sh.n_cand, 1u)] = x;   // (the compiler merges a wave's increments)
+      const uint64_t mask = __ballot(m);
+      const uint32_t slot = wcnt + lanes_below(mask);
+      if (keep && m && slot < (uint32_t)kTkCandPerWave) sh.cand[wave * kTkCandPerWave + slot] = x;
+      wcnt += (uint32_t)__builtin_popcountll(mask);
     }
   }
+  if (lane_id() == 0) sh.wave_cand[wave] = wcnt;
   __syncthreads();
   select_bin(sh, kTkBins, need, 1, &bin, &above);
   prefix = (prefix << 12) | bin;
@@ -223,10 +238,13 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
   // ---- level 2 (bits 7..0) among keys whose top 24 bits equal the prefix ----
   for (int i = tid; i < 256; i += kTkThreads) sh.hist[i] = 0;
   __syncthreads();
-  if (keep) {
-    const uint32_t nc = sh.n_cand;
-    for (uint32_t i = tid; i < nc; i += kTkThreads) {
-      const uint32_t u = sh.cand[i];
+  bool kept = keep;
+#pragma unroll
+  for (int w = 0; w < kTkWaves; ++w) kept = kept && sh.wave_cand[w] <= (uint32_t)kTkCandPerWave;
+  if (kept) {
+    const uint32_t nc = sh.wave_cand[wave];            // wave w scans wave w's slots
+    for (uint32_t i = lane_id(); i < nc; i += kWave) {
+      const uint32_t u = sh.cand[wave * kTkCandPerWave + i];
       if ((u >> 8) == prefix) atomicAdd(&sh.hist[u & 0xffu], 1u);
     }
   } else {
@@ -283,9 +301,12 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
     *eqm = (((uint64_t)q1 << 32) | q0) & vmask;
   };
   uint32_t cgt = 0, ceq = 0;
+  uint64_t gtm0 = 0, eqm0 = 0;                          // cached rows: the run's only block, kept for the write
   for (int p0 = run0; p0 < run0 + run_len && p0 < n; p0 += 64) {
     uint64_t gtm, eqm;
     masks64(p0, &gtm, &eqm);
+    gtm0 = gtm;
+    eqm0 = eqm;
     cgt += (uint32_t)__builtin_popcountll(gtm);
     ceq += (uint32_t)__builtin_popcountll(eqm);
   }
@@ -296,8 +317,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
   uint32_t slot = (gt_incl - cgt) + (eq_before < need ? eq_before : need);
   if (cgt + ceq) {
     for (int p0 = run0; p0 < run0 + run_len && p0 < n; p0 += 64) {
-      uint64_t gtm, eqm;
-      masks64(p0, &gtm, &eqm);
+      uint64_t gtm = gtm0, eqm = eqm0;
+      if (!cached) masks64(p0, &gtm, &eqm);
       // the first (need - eq_before) ties of the block are winners
       uint64_t win = gtm;
       for (uint32_t r = eq_before; r < need && eqm; ++r) {
