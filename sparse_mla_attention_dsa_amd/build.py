@@ -32,9 +32,11 @@ COMMON_FLAGS = [
 # Per-source code generation options. The sparse attention kernel keeps its
 # output accumulator in VGPRs (its rare rescale is VALU work on it) while q
 # lives in AGPRs, and its LDS reads are scheduled as clauses ahead of the MFMAs.
+# The indexer's MFMA results feed VALU epilogues directly from VGPRs.
 SOURCE_FLAGS = {
     "sparse_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1",
                        "-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
+    "indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

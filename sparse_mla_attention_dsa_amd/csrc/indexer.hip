@@ -35,6 +35,14 @@ __device__ __forceinline__ f32x4 mfma_fp8_16x16x128(const i32x8& a, const i32x8&
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// sum of v over lanes l, l ^ 16, l ^ 32, l ^ 48, with the gfx950 lane swaps (VALU, no LDS)
+__device__ __forceinline__ float sum_over_groups(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __global__ __launch_bounds__(64 * kIdxWaves) void indexer_fp8_kernel(IndexerParams p) {
   __shared__ i32x8 q_lds[kIdxHeads * kIdxDim / 32];   // the row's q, 8 KB
   const BatchView& bv = p.batch;
@@ -313,6 +321,262 @@ __global__ __launch_bounds__(kStreamThreads) void indexer_fp8_stream_kernel(Inde
   }
 }
 
+// Prefill rows (cu_seqlens given, up to 1024 requests): MFMA-bound, so the
+// work-group is a tile of 8 query rows of one request x 2048 keys. Keys stream
+// through a two-slot LDS ring in stages of 256 (16 groups of 16, copied with
+// global_load_lds; every wave copies four groups and their 64 scales); each
+// wave holds the q of two rows in registers and runs every key group against
+// both, so one LDS operand read feeds eight MFMAs. Inside a group the 16-byte
+// chunk x of key c sits at chunk 16x + c: the sixteen keys' chunk x are one
+// contiguous 256 B run, which the operand reads take at the linear LDS rate.
+// The MFMA contraction order inside a lane group is free as long as both
+// operands use the same one: lane (c, g) holds bytes [16g, 16g+16) and
+// [64+16g, 64+16g+16) of its head (A) and of its key (B).
+//
+// Per 16-key group and row the epilogue (relu, head weight, head sum) costs
+// about as many VALU cycles as the four MFMAs, so the group loop is software
+// pipelined: the MFMAs of group i+1 are interleaved with the epilogue of
+// group i, whose results they do not touch. relu is an integer max with 0 on
+// the float's bits (negative floats are negative integers), which needs no NaN
+// quieting. The two rows' head sums share one pair of lane swaps: after them
+// lane group g holds row g & 1's total.
+constexpr int kPfThreads = 256;
+constexpr int kPfWaves = kPfThreads / kWave;                     // 4
+constexpr int kPfRowsW = 2;                                      // query rows per wave
+constexpr int kPfRows = kPfWaves * kPfRowsW;                     // 8 rows per work-group
+constexpr int kPfStageGroups = 16;                               // 16-key groups per stage
+constexpr int kPfStageKeys = 16 * kPfStageGroups;                // 256
+constexpr int kPfChunk = 2048;                                   // keys per work-group
+constexpr int kPfStages = kPfChunk / kPfStageKeys;               // 8
+constexpr int kPfChunkGroups = kPfChunk / 16;                    // 128
+constexpr int kPfMaxSeqs = 1024;
+constexpr int64_t kPfMaxStride = 1 << 26;                        // two rows' bytes stay below 2^31
+
+struct PfShared {
+  alignas(16) uint8_t keys[2][kPfStageGroups][16 * kIdxDim];   // 2 x 32 KB
+  alignas(16) float scale[2][kPfStageKeys];                      // 2 x 1 KB
+  alignas(16) int gpage[kPfChunkGroups];                         // page of each group, -1 = masked
+  int blk[kPfMaxSeqs + 1];                                       // row-block prefix over requests
+  int wsum[kPfWaves];
+};
+
+__device__ __forceinline__ float relu_bits(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
+// 4 bytes per lane from global memory straight into LDS at M0 + 4 l.
+__device__ __forceinline__ void lds_dma4(const void* gsrc, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(gsrc), "s"(lds_addr) : "memory", "m0");
+}
+
+__global__ __launch_bounds__(kPfThreads) void indexer_fp8_prefill_kernel(IndexerParams p) {
+  __shared__ PfShared sh;
+  const BatchView& bv = p.batch;
+  const int B = bv.num_seqs;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(wave_id());
+  const int g = lane >> 4, c = lane & 15;
+  const int P = bv.page_size;
+
+  // ---- row blocks of 8 per request, prefix over requests ----
+  int carry = 0;
+  for (int base = 0; base < B; base += kPfThreads) {
+    const int b = base + tid;
+    const int ql = b < B ? bv.cu_seqlens_q[b + 1] - bv.cu_seqlens_q[b] : 0;
+    const int cnt = ql > 0 ? (ql + kPfRows - 1) / kPfRows : 0;
+    const int incl = (int)wave_inclusive_scan((uint32_t)cnt);
+    if (lane == kWave - 1) sh.wsum[wave] = incl;
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kPfWaves; ++w) {
+      const int v = sh.wsum[w];
+      before += (w < wave) ? v : 0;
+      tot += v;
+    }
+    if (b < B) sh.blk[b + 1] = carry + before + incl;
+    carry += tot;
+    __syncthreads();
+  }
+  if (tid == 0) sh.blk[0] = 0;
+  __syncthreads();
+  const int x = blockIdx.x;
+  if (x >= sh.blk[B]) return;
+  int b = 0;
+  {
+    int lo = 0, hi = B - 1;                                      // largest b with blk[b] <= x
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sh.blk[mid] <= x) lo = mid; else hi = mid - 1;
+    }
+    b = lo;
+  }
+  const int q0 = bv.cu_seqlens_q[b];
+  const int q_len = bv.cu_seqlens_q[b + 1] - q0;
+  const int j0 = (x - sh.blk[b]) * kPfRows;                      // first row of the block inside the request
+  int cap = bv.max_pages_per_seq * P;
+  if (cap > bv.max_seq_len_k) cap = bv.max_seq_len_k;
+  if ((int64_t)cap > p.stride) cap = (int)p.stride;
+  const int seq_len = bv.seq_lens_k[b];
+  const int last = min(j0 + kPfRows, q_len) - 1;
+  const int vis_max = visible_keys(seq_len, q_len, last, cap);  // the block's last row sees the most keys
+  const int k0 = blockIdx.y * kPfChunk;
+  if (k0 >= vis_max) return;
+  const int n_stages = min(kPfStages, (vis_max - k0 + kPfStageKeys - 1) / kPfStageKeys);
+  const int32_t* bt = bv.block_table + (int64_t)b * bv.max_pages_per_seq;
+  const int64_t scale_off = (int64_t)P * kIdxDim;
+
+  // page of every 16-key group of the chunk (P is a multiple of 16, so a
+  // group never straddles pages); -1 past the last visible key or for a page
+  // id outside the cache
+  if (tid < kPfChunkGroups) {
+    const int key0 = k0 + 16 * tid;
+    int pg = bt[min(key0, cap - 1) / P];
+    pg = (key0 < vis_max && pg >= 0 && pg < bv.num_pages) ? pg : -1;
+    sh.gpage[tid] = pg;
+  }
+
+  // this wave's two rows: q operands, head weights, visible keys
+  i32x8 qa[kPfRowsW][4];
+  float wv[kPfRowsW][16];
+  int vis[kPfRowsW];
+#pragma unroll
+  for (int r = 0; r < kPfRowsW; ++r) {
+    const int j = min(j0 + kPfRowsW * wave + r, q_len - 1);     // rows past the request repeat its last row
+    vis[r] = (j0 + kPfRowsW * wave + r < q_len) ? visible_keys(seq_len, q_len, j, cap) : 0;
+    const int t = q0 + j;
+    const uint8_t* qr = static_cast<const uint8_t*>(p.q) + (int64_t)t * (kIdxHeads * kIdxDim);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(qr + (16 * m + c) * kIdxDim + 16 * g);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(qr + (16 * m + c) * kIdxDim + 64 + 16 * g);
+      qa[r][m] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    const float* wrow = p.w + (int64_t)t * kIdxHeads;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const f32x4 w4 = *reinterpret_cast<const f32x4*>(wrow + 16 * m + 4 * g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[r][4 * m + i] = w4[i];
+    }
+  }
+  // Consume q and the weights here so that no compiler-placed vector-memory
+  // wait inside the loop also drains the (to the compiler invisible) copies.
+#pragma unroll
+  for (int r = 0; r < kPfRowsW; ++r) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) asm volatile("" :: "v"(qa[r][m]));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) asm volatile("" :: "v"(wv[r][i]));
+  }
+
+  // Output: lane group g < 2 stores row g of the wave through a buffer
+  // resource over the wave's two rows; out-of-range offsets drop the store.
+  constexpr uint32_t kDrop = 0x80000000u;
+  const int64_t row_w = (int64_t)q0 + j0 + kPfRowsW * wave;      // may lie past the batch: then vis = 0
+  const __amdgpu_buffer_rsrc_t out_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      p.logits + row_w * p.stride, (short)0, (int)(2 * p.stride * 4), 0x00020000);
+  const int vis_g = g == 0 ? vis[0] : (g == 1 ? vis[1] : 0);
+  const uint32_t row_off = (uint32_t)(g & 1) * (uint32_t)p.stride * 4u;
+
+  // copies of stage st into slot st & 1: wave w copies groups 4w .. 4w+3
+  // (two 1 KB copies each; copy h: lane l fetches chunk (64h + l) >> 4 of key
+  // (64h + l) & 15) and their scales (lane l: key l & 15 of group 4w + l / 16)
+  const uint8_t* cache = p.cache;
+  auto issue_stage = [&](int st) {
+    const int gb = st * kPfStageGroups + 4 * wave;               // first group of this wave in the chunk
+    const i32x4 pg4 = *reinterpret_cast<const i32x4*>(&sh.gpage[gb]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int key0 = k0 + 16 * (gb + u);
+      const int pg = max(pg4[u], 0);                             // masked groups copy page 0; not stored
+      const uint8_t* src = cache + (int64_t)pg * p.page_bytes + (int64_t)(key0 % P) * kIdxDim;
+      const uint32_t dst = lds_offset(sh.keys[st & 1][4 * wave + u]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int L = 64 * h + lane;
+        lds_dma16(src + (L & 15) * kIdxDim + 16 * (L >> 4), dst + 1024 * h);
+      }
+    }
+    const int my = max(sh.gpage[gb + g], 0);
+    const int key0 = k0 + 16 * (gb + g);
+    lds_dma4(cache + (int64_t)my * p.page_bytes + scale_off + 4 * (key0 % P + c),
+             lds_offset(&sh.scale[st & 1][64 * wave]));
+  };
+
+  const int kof0 = (16 * g + c) * 16;                           // chunk g of key c
+  const int kof1 = (16 * (g + 4) + c) * 16;                     // chunk g + 4 of key c
+  __syncthreads();                                               // page table visible
+  issue_stage(0);
+  for (int st = 0; st < n_stages; ++st) {
+    wait_vmcnt<0>();                                             // own copies of stage st (and stores)
+    __syncthreads();                                             // everyone's copies; slot st+1 free
+    if (st + 1 < n_stages) issue_stage(st + 1);
+    const int slot = st & 1;
+    const int kst = k0 + st * kPfStageKeys;
+    const uint64_t valid = __ballot(lane < kPfStageGroups && sh.gpage[st * kPfStageGroups + c] >= 0);
+    const int lim = vis_g - kst - c;                             // store key 16 i + c of the stage iff 16 i < lim
+    const uint32_t off0 = row_off + 4u * (uint32_t)(kst + c);
+
+    auto read_kb = [&](int grp) -> i32x8 {
+      const uint8_t* kg = sh.keys[slot][grp];
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(kg + kof0);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(kg + kof1);
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    f32x4 acc[2][kPfRowsW][4];
+    auto mfmas = [&](f32x4 (&a)[kPfRowsW][4], const i32x8& kb) {
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < kPfRowsW; ++r)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) a[r][m] = mfma_fp8_16x16x128(qa[r][m], kb, zero);
+    };
+    i32x8 kb_next = read_kb(1);
+    mfmas(acc[0], read_kb(0));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int grp = 0; grp < kPfStageGroups; ++grp) {
+      i32x8 kb_after;
+      if (grp + 2 < kPfStageGroups) kb_after = read_kb(grp + 2);
+      const float sg = sh.scale[slot][16 * grp + c];
+      if (grp + 1 < kPfStageGroups) mfmas(acc[(grp + 1) & 1], kb_next);
+      const f32x4 (&a)[kPfRowsW][4] = acc[grp & 1];
+      float part[kPfRowsW];
+#pragma unroll
+      for (int r = 0; r < kPfRowsW; ++r) {
+        float s = wv[r][0] * relu_bits(a[r][0][0]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int i = (m == 0 ? 1 : 0); i < 4; ++i) s = fmaf(wv[r][4 * m + i], relu_bits(a[r][m][i]), s);
+        part[r] = s;
+      }
+      // lane swaps: rows 0/1 of groups (0,1) and (2,3), then the halves
+      const auto sw16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part[0]), __float_as_uint(part[1]),
+                                                         false, false);
+      const float h = __uint_as_float(sw16[0]) + __uint_as_float(sw16[1]);
+      const auto sw32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(h), __float_as_uint(h), false, false);
+      const float tot = (__uint_as_float(sw32[0]) + __uint_as_float(sw32[1])) * sg;
+      const float val = ((valid >> grp) & 1) ? tot : -INFINITY;
+      const uint32_t off = (16 * grp < lim) ? off0 : kDrop;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), out_rsrc, (int)(off + 64u * grp), 0, 0);
+      if (grp + 2 < kPfStageGroups) kb_next = kb_after;
+      // issue order: operand reads, then each MFMA followed by a slice of the epilogue
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  wait_vmcnt<0>();
+}
+
 // fp32 keys (H <= 64, D <= 128): one thread per key, q of the row staged in LDS.
 constexpr int kF32Block = 256;
 
@@ -363,6 +627,13 @@ hipError_t launch_indexer_fp8(const IndexerParams& p, hipStream_t s) {
     if (wgs > 768) wgs = 768;
     if (wgs < 1) wgs = 1;
     hipLaunchKernelGGL(indexer_fp8_stream_kernel, dim3((unsigned)wgs), dim3(kStreamThreads), 0, s, p);
+    return hipGetLastError();
+  }
+  if (p.batch.cu_seqlens_q != nullptr && p.batch.num_seqs <= kPfMaxSeqs && p.stride <= kPfMaxStride) {
+    // row blocks: sum over requests of ceil(q_len / 8) <= num_rows / 8 + num_seqs
+    const int blocks = (p.batch.num_rows + kPfRows - 1) / kPfRows + p.batch.num_seqs;
+    dim3 grid(blocks, (p.batch.max_seq_len_k + kPfChunk - 1) / kPfChunk);
+    hipLaunchKernelGGL(indexer_fp8_prefill_kernel, grid, dim3(kPfThreads), 0, s, p);
     return hipGetLastError();
   }
   dim3 grid(p.batch.num_rows, chunks);

@@ -61,6 +61,8 @@ SMALL = [
     small_config("pre2_p64", seed=104, lens=[300, 2500], q_lens=[37, 64]),
     small_config("pre2_k128", seed=105, lens=[400, 1000], q_lens=[50, 21], topk=128),
     small_config("pre1_k4096", seed=106, lens=[5000], q_lens=[40], topk=4096),
+    small_config("pre3_p16_ragged", seed=109, lens=[900, 64, 3000], q_lens=[17, 1, 100], page_size=16,
+                 topk=512),
     small_config("dec_f32", seed=107, lens=[90, 300], page_size=16, topk=64, idx_kind="f32", mla_kind="f32"),
     small_config("pre_f32", seed=108, lens=[120, 77], q_lens=[9, 13], page_size=16, topk=32,
                  idx_kind="f32", mla_kind="f32"),
