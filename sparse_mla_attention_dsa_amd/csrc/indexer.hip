@@ -7,7 +7,7 @@
 // paged MQA-logits kernel; forward_indexer gives the same score per request.)
 //
 // fp8 path (H = 64, D = 128): the q . k contraction runs on the gfx950 fp8 MFMA
-// v_mfma_scale_f32_16x16x128_f8f6f4 with unit block scales. Heads are the M
+// v_mfma_f32_16x16x128_f8f6f4 (no block scales). Heads are the M
 // dimension and keys the N dimension, so one 16x16 accumulator holds 16 heads x
 // 16 keys and each lane ends up with 16 heads of a single key: relu, head weight
 // and the head sum are lane-local, followed by two cross-lane adds. sigma >= 0
@@ -31,8 +31,17 @@ constexpr int kIdxGroupsPerWave = 8;                               // 16 keys ea
 constexpr int kIdxChunk = 16 * kIdxGroupsPerWave * kIdxWaves;      // 512 keys per work-group
 
 __device__ __forceinline__ f32x4 mfma_fp8_16x16x128(const i32x8& a, const i32x8& b, const f32x4& c) {
-  // format 0 = fp8 e4m3 for both operands; E8M0 scale 127 = 2^0 for both.
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  // format 0 = fp8 e4m3 for both operands, no block scales: all-zero scale
+  // operands select the unscaled v_mfma_f32_16x16x128_f8f6f4, which computes
+  // the plain fp8 product (the same values as unit E8M0 scales) and lets the
+  // wave issue independent VALU work under it far better than the scaled form.
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// relu as an integer max with 0 on the float's bits (negative floats are
+// negative integers): one VALU op, no NaN quieting as fmaxf needs
+__device__ __forceinline__ float relu_bits(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
 }
 
 // sum of v over lanes l, l ^ 16, l ^ 32, l ^ 48, with the gfx950 lane swaps (VALU, no LDS)
@@ -124,7 +133,7 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_fp8_kernel(IndexerPara
     for (int m = 0; m < 4; ++m) {
       const f32x4 acc = mfma_fp8_16x16x128(qa[m], kb[u], zero);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) part = fmaf(wv[4 * m + i], fmaxf(acc[i], 0.f), part);
+      for (int i = 0; i < 4; ++i) part = fmaf(wv[4 * m + i], relu_bits(acc[i]), part);
     }
     part += shfl_xor_f(part, 16);
     part += shfl_xor_f(part, 32);
@@ -306,7 +315,7 @@ __global__ __launch_bounds__(kStreamThreads) void indexer_fp8_stream_kernel(Inde
         for (int m = 0; m < 4; ++m) {
           const f32x4 acc = mfma_fp8_16x16x128(qa[m], k0[u], zero);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) part = fmaf(wv[4 * m + i], fmaxf(acc[i], 0.f), part);
+          for (int i = 0; i < 4; ++i) part = fmaf(wv[4 * m + i], relu_bits(acc[i]), part);
         }
         part += shfl_xor_f(part, 16);
         part += shfl_xor_f(part, 32);
@@ -359,10 +368,6 @@ struct PfShared {
   int blk[kPfMaxSeqs + 1];                                       // row-block prefix over requests
   int wsum[kPfWaves];
 };
-
-__device__ __forceinline__ float relu_bits(float x) {
-  return __int_as_float(max(__float_as_int(x), 0));
-}
 
 // 4 bytes per lane from global memory straight into LDS at M0 + 4 l.
 __device__ __forceinline__ void lds_dma4(const void* gsrc, uint32_t lds_addr) {
@@ -462,16 +467,6 @@ __global__ __launch_bounds__(kPfThreads) void indexer_fp8_prefill_kernel(Indexer
       for (int i = 0; i < 4; ++i) wv[r][4 * m + i] = w4[i];
     }
   }
-  // Consume q and the weights here so that no compiler-placed vector-memory
-  // wait inside the loop also drains the (to the compiler invisible) copies.
-#pragma unroll
-  for (int r = 0; r < kPfRowsW; ++r) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) asm volatile("" :: "v"(qa[r][m]));
-#pragma unroll
-    for (int i = 0; i < 16; ++i) asm volatile("" :: "v"(wv[r][i]));
-  }
-
   // Output: lane group g < 2 stores row g of the wave through a buffer
   // resource over the wave's two rows; out-of-range offsets drop the store.
   constexpr uint32_t kDrop = 0x80000000u;
@@ -510,49 +505,81 @@ __global__ __launch_bounds__(kPfThreads) void indexer_fp8_prefill_kernel(Indexer
   const int kof1 = (16 * (g + 4) + c) * 16;                     // chunk g + 4 of key c
   __syncthreads();                                               // page table visible
   issue_stage(0);
+  if (n_stages > 1) issue_stage(1);
+  // Consume q and the weights only now: their loads overlap the page lookups
+  // and the first copies, and no compiler-placed vector-memory wait inside the
+  // loop drains the (to the compiler invisible) copies.
+#pragma unroll
+  for (int r = 0; r < kPfRowsW; ++r) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) asm volatile("" :: "v"(qa[r][m]));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) asm volatile("" :: "v"(wv[r][i]));
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // One software pipeline over all groups of the chunk: iteration i issues
+  // the MFMAs of group i + 1 and runs the epilogue of group i. The stage
+  // boundary sits in the last iteration of a stage, before the MFMAs of the
+  // next stage's first group: wait for the next stage's copies, barrier (every
+  // wave has read this stage's operands and scales), then start the copies of
+  // the stage after into the slot just released. Vector-memory operations
+  // complete in issue order, so the copies issued at the previous boundary are
+  // done once at most the stores issued since (one per iteration, at least 15)
+  // are outstanding.
+  auto read_kb = [&](int slot, int grp) -> i32x8 {
+    const uint8_t* kg = sh.keys[slot][grp];
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(kg + kof0);
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(kg + kof1);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  f32x4 acc[2][kPfRowsW][4];
+  auto mfmas = [&](f32x4 (&a)[kPfRowsW][4], const i32x8& kb) {
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < kPfRowsW; ++r)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) a[r][m] = mfma_fp8_16x16x128(qa[r][m], kb, zero);
+  };
+  i32x8 kb_next = read_kb(0, 1);
+  mfmas(acc[0], read_kb(0, 0));
+  __builtin_amdgcn_sched_barrier(0);
   for (int st = 0; st < n_stages; ++st) {
-    wait_vmcnt<0>();                                             // own copies of stage st (and stores)
-    __syncthreads();                                             // everyone's copies; slot st+1 free
-    if (st + 1 < n_stages) issue_stage(st + 1);
     const int slot = st & 1;
     const int kst = k0 + st * kPfStageKeys;
     const uint64_t valid = __ballot(lane < kPfStageGroups && sh.gpage[st * kPfStageGroups + c] >= 0);
     const int lim = vis_g - kst - c;                             // store key 16 i + c of the stage iff 16 i < lim
     const uint32_t off0 = row_off + 4u * (uint32_t)(kst + c);
-
-    auto read_kb = [&](int grp) -> i32x8 {
-      const uint8_t* kg = sh.keys[slot][grp];
-      const i32x4 lo = *reinterpret_cast<const i32x4*>(kg + kof0);
-      const i32x4 hi = *reinterpret_cast<const i32x4*>(kg + kof1);
-      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    };
-    f32x4 acc[2][kPfRowsW][4];
-    auto mfmas = [&](f32x4 (&a)[kPfRowsW][4], const i32x8& kb) {
-      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int r = 0; r < kPfRowsW; ++r)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) a[r][m] = mfma_fp8_16x16x128(qa[r][m], kb, zero);
-    };
-    i32x8 kb_next = read_kb(1);
-    mfmas(acc[0], read_kb(0));
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int grp = 0; grp < kPfStageGroups; ++grp) {
-      i32x8 kb_after;
-      if (grp + 2 < kPfStageGroups) kb_after = read_kb(grp + 2);
       const float sg = sh.scale[slot][16 * grp + c];
-      if (grp + 1 < kPfStageGroups) mfmas(acc[(grp + 1) & 1], kb_next);
+      i32x8 kb_after;
+      if (grp + 2 < kPfStageGroups) {
+        kb_after = read_kb(slot, grp + 2);
+        mfmas(acc[(grp + 1) & 1], kb_next);
+      } else if (grp + 2 == kPfStageGroups) {
+        mfmas(acc[(grp + 1) & 1], kb_next);
+      } else {
+        // stage boundary (on the last stage the next-group MFMAs run on a
+        // stale slot and are never used)
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");      // own reads of this slot done
+        wait_vmcnt<15>();
+        __syncthreads();
+        if (st + 2 < n_stages) issue_stage(st + 2);
+        kb_next = read_kb(slot ^ 1, 1);
+        mfmas(acc[0], read_kb(slot ^ 1, 0));
+      }
       const f32x4 (&a)[kPfRowsW][4] = acc[grp & 1];
       float part[kPfRowsW];
 #pragma unroll
       for (int r = 0; r < kPfRowsW; ++r) {
-        float s = wv[r][0] * relu_bits(a[r][0][0]);
+        float sum = wv[r][0] * relu_bits(a[r][0][0]);
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
-          for (int i = (m == 0 ? 1 : 0); i < 4; ++i) s = fmaf(wv[r][4 * m + i], relu_bits(a[r][m][i]), s);
-        part[r] = s;
+          for (int i = (m == 0 ? 1 : 0); i < 4; ++i) sum = fmaf(wv[r][4 * m + i], relu_bits(a[r][m][i]), sum);
+        part[r] = sum;
       }
       // lane swaps: rows 0/1 of groups (0,1) and (2,3), then the halves
       const auto sw16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part[0]), __float_as_uint(part[1]),
