@@ -10,75 +10,92 @@
 //   z_i = scale * (q[t,h] . C_i),  out[t,h] = sum_i softmax(z)_i C_i[:512],
 //   lse[t,h] = log sum_i exp(z_i).
 //
-// bf16 path (Dl = 512, Dr = 64, Hm a multiple of 64). One work-group of four
-// waves (one per SIMD) handles one (row, split of the top-k list, group of 64
-// heads); wave w owns heads 16w .. 16w+15 of the group outright, so scores,
-// softmax and P.V of those heads never leave the wave:
-//   * the split's positions are resolved once through the block table into
-//     cache-row ids in LDS, skipping -1 / out-of-range entries (so the -1 tail
-//     of short rows costs nothing);
-//   * gathered rows arrive 32 at a time straight from HBM into a ring of four
-//     LDS tiles (global_load_lds, 16 bytes per lane, no register staging); two
-//     tiles are in flight while one is scored and the previous one multiplied
-//     into the output. Rows are stored dense with an XOR swizzle of their
-//     16-byte chunks, which keeps both LDS read patterns below free of bank
-//     conflicts;
-//   * scores: S^T[32 rows x 16 heads] = C_tile . Q^T over the 576-wide
-//     contraction with v_mfma_f32_16x16x32_bf16 (rows = M from LDS, heads = N:
-//     the wave keeps its 16 heads x 576 of q in registers);
-//   * online softmax in fp32, base 2, with lazy rescaling: the running maximum
-//     of a head only moves when a tile exceeds it by more than 2^8, so the
-//     accumulator rescale is skipped on most tiles;
-//   * the score accumulator of lane (c, g) holds head c at rows {4g+i, 16+4g+i},
-//     which is exactly the A operand (head c, eight rows of the contraction)
-//     of O[16 heads x 512] += P . V_tile, so P goes from registers to the MFMA
-//     without an LDS round trip. V arrives as the B operand through the gfx950
-//     transposing LDS read (ds_read_b64_tr_b16), two per 16 value columns;
-//   * the scores of tile j + 1 are issued before the softmax and P.V of tile j,
-//     so the wave has MFMA work while its softmax runs;
-//   * single split: out = O / l in bf16 and lse; several splits: fp32 partials
-//     (O / l, lse) merged by mla_combine_kernel.
-// Work-groups are ordered so that the head groups of one (row, split) unit, and
-// neighbouring units, land on the same XCD (work-group i runs on XCD i % 8) and
-// share the gathered rows through that XCD's L2.
+// bf16 path (Dl = 512, Dr = 64, Hm a multiple of 64). One work-group of eight
+// waves handles one (row, split of the top-k list, group of 64 heads).
+// Gathered rows arrive 32 at a time (a tile) straight from HBM into a ring of
+// four LDS slots (global_load_lds, 16 bytes per lane, no register staging),
+// XOR-swizzled by 16-byte chunk. The waves have two roles, one wave of each
+// per SIMD, so that the stalls of one (LDS latency, softmax) are covered by the
+// MFMAs of the other:
+//   * score waves 0..3: wave w computes S[32 rows x 16 heads] (heads 16 w ..)
+//     of the next tile over the 576-wide contraction with
+//     v_mfma_f32_16x16x32_bf16 (rows as M from LDS, heads as N from q held in
+//     registers for the whole split), then the online softmax of its heads,
+//     whose rows are all in the wave: fp32, base 2, lazy rescaling (the
+//     running maximum of a head only moves when a tile exceeds it by more than
+//     2^8). The probabilities go to a 4 KB LDS buffer as bf16;
+//   * value waves 4..7: wave 4 + v owns value columns 128 v .. 128 v + 127 of
+//     all 64 heads and computes O^T[128 columns x 64 heads] += V^T . P^T, so
+//     every V element is read from LDS once per tile. V^T arrives as the A
+//     operand through the gfx950 transposing LDS read (ds_read_b64_tr_b16),
+//     P^T as the B operand from the probability buffer. The accumulator gives
+//     each lane four consecutive columns of one head, so the output leaves in
+//     8- or 16-byte stores.
+// Every wave issues a share of the tile copies, spread over its MFMAs.
+//
+// Interval j (between two barriers B2): the score waves compute S and the
+// softmax of tile j+1 while the value waves, having read P of tile j into
+// registers, multiply tile j; all waves spread their copies of tile j+3 (into
+// the slot of tile j-1, which no wave reads any more) over their MFMAs;
+// barrier B1; the score waves write P of tile j+1; every wave waits for its
+// copies of tile j+2; barrier B2.
+//
+// Single split: out = O / l in bf16 and lse; several splits: fp32 partials
+// (O / l, lse) merged by mla_combine_kernel. Work-groups are ordered so that
+// the head groups of one (row, split) unit, and neighbouring units, land on
+// the same XCD (work-group i runs on XCD i % 8) and share the gathered rows
+// through that XCD's L2.
 #include "device_common.h"
 #include "dsa_internal.h"
 
 namespace dsa {
 namespace {
 
-constexpr int kMlaThreads = 256;
-constexpr int kMlaWaves = kMlaThreads / kWave;          // 4
+constexpr int kMlaThreads = 512;
+constexpr int kMlaWaves = kMlaThreads / kWave;          // 8
+constexpr int kRoleWaves = kMlaWaves / 2;               // 4 score waves, 4 value waves
 constexpr int kRowBytes = kMlaDqk * 2;                  // 1152: one cached latent row
 constexpr int kChunksPerRow = kRowBytes / 16;           // 72 chunks of 16 bytes
 constexpr int kTileBytes = kMlaTile * kRowBytes;        // 36864
 constexpr int kPiecesPerTile = kTileBytes / 1024;       // 36 wave-wide 1 KB copies
-constexpr int kPiecesPerWave = kPiecesPerTile / kMlaWaves;   // 9
+constexpr int kPiecesMax = (kPiecesPerTile + kMlaWaves - 1) / kMlaWaves;   // 5 (waves 0..3), else 4
 constexpr int kRing = 4;                                // LDS tile slots
-constexpr int kEntriesPerThread = kMlaMaxEntriesPerBlock / kMlaThreads;  // 8
+constexpr int kEntriesPerThread = kMlaMaxEntriesPerBlock / kMlaThreads;  // 4
 constexpr int kKSteps = kMlaDqk / 32;                   // 18 K-steps of 32
-constexpr int kVTiles = kMlaDl / 16;                    // 32 value-column tiles
+constexpr int kKB = 2;                                  // K-steps per score operand batch
+constexpr int kKBatches = kKSteps / kKB;                // 9
+constexpr int kPvNT = kMlaDl / kRoleWaves / 16;         // 8 value-column tiles per value wave
+constexpr int kPvHT = kMlaHeadsPerGroup / 16;           // 4 head tiles
+constexpr int kSAhead = 3;                              // score operand batches read ahead of their MFMAs
+constexpr int kVAhead = 4;                              // value-column tiles read ahead of their MFMAs
 constexpr float kRescaleThreshold = 8.0f;               // log2 units
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+static_assert(kPiecesPerTile > (kPiecesMax - 1) * kMlaWaves && kPiecesPerTile <= kPiecesMax * kRoleWaves + (kPiecesMax - 1) * kRoleWaves,
+              "waves 0..3 copy kPiecesMax pieces of a tile, waves 4..7 one fewer");
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 struct MlaShared {
   // Gathered rows, dense (1152 B per row). Inside row r the 16-byte chunk c is
   // stored at chunk position c ^ swz(r) (see swz).
   alignas(16) uint8_t kv[kRing][kTileBytes];
+  // P of one tile, [head][contraction index] bf16: row 4g + i of the tile at
+  // index 8g + i, row 16 + 4g + i at index 8g + 4 + i (the order in which the
+  // value waves' transposing reads deliver V)
+  alignas(16) uint16_t p[kMlaHeadsPerGroup * kMlaTile];
+  alignas(16) float alpha[kMlaHeadsPerGroup];            // rescale factor of the tile; at the end 1 / l
+  alignas(16) int flag[kRoleWaves];                      // some head of score wave w rescaled
   int32_t rowid[kMlaMaxEntriesPerBlock];
   int wave_sum[kMlaWaves];
 };
 
 // Chunk swizzle of row r: the low three bits of r. With it the score operand
 // reads (sixteen rows, one logical chunk each) and the transposed value reads
-// (sixteen rows x 32 bytes) both run at the conflict-free LDS rate (measured on
-// gfx950; rows are 1152 bytes apart). Rows r and r + 16 share the swizzle.
+// (rows 4g .. 4g+3, 32 bytes each, per 16-lane block g) run at the full LDS
+// rate (measured on gfx950; rows are 1152 bytes apart).
 __device__ __forceinline__ int swz(int row) { return row & 7; }
 
 // max / sum of v over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups),
@@ -108,6 +125,21 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
 }
 
+// Wait until at most `tiles` tiles of this wave's copies are outstanding
+// (vector-memory operations complete in issue order; a wave copies kPiecesMax
+// or kPiecesMax - 1 pieces per tile).
+__device__ __forceinline__ void wait_tiles(int tiles, bool five) {
+  if (five) {
+    if (tiles >= 2) wait_vmcnt<2 * kPiecesMax>();
+    else if (tiles == 1) wait_vmcnt<kPiecesMax>();
+    else wait_vmcnt<0>();
+  } else {
+    if (tiles >= 2) wait_vmcnt<2 * (kPiecesMax - 1)>();
+    else if (tiles == 1) wait_vmcnt<kPiecesMax - 1>();
+    else wait_vmcnt<0>();
+  }
+}
+
 __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
   __shared__ MlaShared sh;
   const BatchView& bv = p.batch;
@@ -132,6 +164,9 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(wave_id());
   const int g = lane >> 4, c = lane & 15;
+  const bool scorer = wave < kRoleWaves;     // uniform per wave
+  const int rw = wave & (kRoleWaves - 1);    // index inside the role
+  const bool five = wave + kMlaWaves * (kPiecesMax - 1) < kPiecesPerTile;   // copies kPiecesMax pieces
 
   int b, jrow, q_len;
   row_to_seq(t, bv.cu_seqlens_q, bv.num_seqs, &b, &jrow, &q_len);
@@ -141,8 +176,9 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
   if (seq_len > addressable) seq_len = addressable;
   const int32_t* bt = bv.block_table + (int64_t)b * bv.max_pages_per_seq;
 
-  const int head0 = hg * kMlaHeadsPerGroup + 16 * wave;   // this wave's first head
   const int Hm = p.heads;
+  const int hbase = hg * kMlaHeadsPerGroup;  // first head of the group
+  const int hl_s = 16 * rw + c;              // score waves: this lane's head inside the group
 
   // ---- resolve this split's entries into cache-row ids (compacted, in order) ----
   const int e_begin = s * p.entries_per_split;
@@ -161,13 +197,6 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
     const bool in = pos[q] >= 0 && pos[q] < seq_len;
     page[q] = in ? bt[pos[q] / P] : -1;
   }
-  // q (head c of the wave, all 576: the N operand) is fetched after the page
-  // lookups so that waiting for those (vector loads complete in order) does not
-  // also wait for q
-  const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + ((int64_t)t * Hm + head0 + c) * kMlaDqk;
-  bf16x8 qf[kKSteps];
-#pragma unroll
-  for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks + 8 * g);
   int nmine = 0;
 #pragma unroll
   for (int q = 0; q < kEntriesPerThread; ++q) nmine += (page[q] >= 0 && page[q] < bv.num_pages) ? 1 : 0;
@@ -193,245 +222,284 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
   const uint8_t* kvbase = static_cast<const uint8_t*>(p.kv);
   const int n_tiles = (nvalid + kMlaTile - 1) / kMlaTile;
 
-  // A tile is 36 copies of 1 KB; copy i = wave + 4j covers LDS chunks
-  // 64i .. 64i+63, lane l taking chunk 64i + l of the dense tile: row
+  // ---- copies. A tile is 36 copies of 1 KB; copy i = wave + 8j covers LDS
+  // chunks 64i .. 64i+63, lane l taking chunk 64i + l of the dense tile: row
   // r = chunk / 72, LDS chunk position col = chunk % 72, which holds the
-  // logical chunk col ^ swz(r) of the row.
-  // source row ids of this wave's copies of `tile`
-  auto fetch_rows = [&](int tile, int (&rid)[kPiecesPerWave]) {
+  // logical chunk col ^ swz(r) of the row. Rows past the split's valid
+  // entries re-read its first row (their scores are masked).
+  auto fetch_rows = [&](int tile, int (&rid)[kPiecesMax]) {
 #pragma unroll
-    for (int j = 0; j < kPiecesPerWave; ++j) {
-      const int r = (64 * (wave + kMlaWaves * j) + lane) / kChunksPerRow;
-      const int e = tile * kMlaTile + r;
-      rid[j] = sh.rowid[e < nvalid ? e : 0];   // rows past the end re-read the split's first row (masked)
+    for (int j = 0; j < kPiecesMax; ++j) {
+      const int pc = min(wave + kMlaWaves * j, kPiecesPerTile - 1);
+      const int e = tile * kMlaTile + (64 * pc + lane) / kChunksPerRow;
+      rid[j] = sh.rowid[e < nvalid ? e : 0];
     }
   };
-  // copies j0 .. j1-1 of this wave for `tile`
-  auto issue_pieces = [&](int tile, const int (&rid)[kPiecesPerWave], int j0, int j1) {
+  auto issue_pieces = [&](int tile, const int (&rid)[kPiecesMax], int j0, int j1) {
     const uint32_t dst = lds_offset(sh.kv[tile % kRing]);
 #pragma unroll
     for (int j = j0; j < j1; ++j) {
-      const int chunk = 64 * (wave + kMlaWaves * j) + lane;
+      if (j == kPiecesMax - 1 && !five) break;
+      const int pc = wave + kMlaWaves * j;
+      const int chunk = 64 * pc + lane;
       const int r = chunk / kChunksPerRow;
       const int col = ((chunk - r * kChunksPerRow) ^ swz(r)) * 16;
-      lds_dma16(kvbase + (int64_t)rid[j] * kRowBytes + col, dst + 1024 * (wave + kMlaWaves * j));
+      lds_dma16(kvbase + (int64_t)rid[j] * kRowBytes + col, dst + 1024 * pc);
     }
   };
-  auto issue_tile = [&](int tile) {
-    int rid[kPiecesPerWave];
-    fetch_rows(tile, rid);
-    issue_pieces(tile, rid, 0, kPiecesPerWave);
-  };
 
-  // Consume q here: the compiler then knows its loads have completed, and it
-  // places no vector-memory waits inside the tile loop, where they would also
-  // drain the (to it invisible) tile copies in flight.
-#pragma unroll
-  for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" : "+a"(qf[ks]));
 
-  // score operand (A): lane (c, g) reads row c (and 16 + c) of the tile, 16-byte
-  // chunk 4 ks + g of the row. With ks = 2a + u the swizzled position is
-  // 8a + ((4u + g) ^ swz(c)): a per-lane base plus an immediate.
-  const int sw_c = swz(c);
-  const int a_off0 = c * kRowBytes + (((g) ^ sw_c) << 4);
-  const int a_off1 = c * kRowBytes + (((4 + g) ^ sw_c) << 4);
-  // value operand (B): for rows 16h + 4g + (c >> 2) and value columns
-  // 16nt + 4(c & 3) .. +3; with nt = 4a + u the chunk is 8a + ((2u + ((c & 3) >> 1)) ^ swz(row))
+  // score operand (A): lane (c, g) reads rows c and 16 + c of the tile,
+  // 16-byte chunk 4 ks + g of the row. With ks = 2a + u the swizzled position
+  // is 8a + ((4u + g) ^ swz(row)): a per-lane base plus an immediate.
+  const int a_off0 = c * kRowBytes + ((g ^ swz(c)) << 4);
+  const int a_off1 = c * kRowBytes + (((4 + g) ^ swz(c)) << 4);
+  // value operand (A of O^T += V^T P^T): two transposing reads give lane
+  // (c, g) value column 128 v + 16 nt + c of rows 4g .. 4g+3 and 16+4g ..
+  // 16+4g+3 (contraction index 8g + e, e = 0..7). Lane 4k + m of block g names
+  // row 16h + 4g + k (h = which read), columns 16 nt + 4m .. + 3 of the wave's
+  // 128: logical chunk 16 v + 2 nt + (m >> 1), byte 8 (m & 1). With
+  // nt = 4a + u the chunk sits at 16 v + 8a + ((2u + (m >> 1)) ^ swz(row)).
   int v_off[2][4];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int r = 16 * h + 4 * g + (c >> 2);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      v_off[h][u] = r * kRowBytes + (((2 * u + ((c & 3) >> 1)) ^ swz(r)) << 4) + ((c & 1) << 3);
+      v_off[h][u] = r * kRowBytes + ((16 * rw + ((2 * u + ((c & 3) >> 1)) ^ swz(r))) << 4) + ((c & 1) << 3);
   }
+  // P^T operand (B): lane (c, g) reads P[head 16 hb + c][8g .. 8g+7]
+  const int p_off = c * kMlaTile + 8 * g;
 
-  f32x4 acc_o[kVTiles];   // O[head 4g + i][value column 16 nt + c] (PV accumulator layout)
-#pragma unroll
-  for (int nt = 0; nt < kVTiles; ++nt) acc_o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY;   // running max (log2 units) of head c
-  float l_part = 0.f;        // this lane's share of head c's softmax denominator
+  constexpr int kAhead = kRing - 1;                    // tiles copied ahead of the one scored
+  int rid_next[kPiecesMax];
 
-  // Score operands of K-steps 3b .. 3b+2 (rows c and 16 + c of the tile) and
-  // their MFMAs into S^T: s0 rows 4g+i, s1 rows 16+4g+i, head c.
-  constexpr int kKB = 3;                                 // K-steps per batch
-  constexpr int kKBatches = kKSteps / kKB;               // 6
-  auto read_k = [&](const uint8_t* kvt, int b, bf16x8 (&dst)[kKB][2]) {
-#pragma unroll
-    for (int u = 0; u < kKB; ++u) {
-      const int ks = kKB * b + u;
-      const int off = ((ks & 1) ? a_off1 : a_off0) + 128 * (ks >> 1);
-      dst[u][0] = *reinterpret_cast<const bf16x8*>(kvt + off);
-      dst[u][1] = *reinterpret_cast<const bf16x8*>(kvt + off + 16 * kRowBytes);
+  if (scorer) {
+    // ================= score waves =================
+    // The copies of tile 0, then q (the N operand: lane (c, g) holds head
+    // hbase + hl_s, elements 32 ks + 8 g .. + 7), consumed at once: the
+    // compiler then knows its loads have completed and places no
+    // vector-memory waits inside the tile loop, where they would also drain the
+    // (to it invisible) tile copies in flight. Its wait covers tile 0, which
+    // the scores need first anyway; tiles 1 and 2 follow.
+    if (n_tiles > 0) {
+      fetch_rows(0, rid_next);
+      issue_pieces(0, rid_next, 0, kPiecesMax);
     }
-  };
-  auto mfma_k = [&](int b, const bf16x8 (&op)[kKB][2], f32x4& s0, f32x4& s1) {
+    bf16x8 qf[kKSteps];
+    {
+      const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + ((int64_t)t * Hm + hbase + hl_s) * kMlaDqk;
 #pragma unroll
-    for (int u = 0; u < kKB; ++u) {
-      s0 = mfma_bf16(op[u][0], qf[kKB * b + u], s0);
-      s1 = mfma_bf16(op[u][1], qf[kKB * b + u], s1);
-    }
-  };
-  // value operands of column tiles 8n .. 8n+7 (two transposing reads each)
-  constexpr int kVB = 8;
-  auto read_v = [&](const uint8_t* kvt, int n, i16x4 (&lo)[kVB], i16x4 (&hi)[kVB]) {
+      for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks + 8 * g);
 #pragma unroll
-    for (int u = 0; u < kVB; ++u) {
-      const int nt = kVB * n + u;
-      const int imm = 128 * (nt >> 2);
-      lo[u] = lds_read_tr16(kvt + v_off[0][nt & 3] + imm);
-      hi[u] = lds_read_tr16(kvt + v_off[1][nt & 3] + imm);
+      for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" : "+v"(qf[ks]));
     }
-  };
-  auto scores = [&](int tile, f32x4& s0, f32x4& s1) {   // (prologue only)
-    const uint8_t* kvt = sh.kv[tile % kRing];
-    s0 = f32x4{0.f, 0.f, 0.f, 0.f};
-    s1 = s0;
-#pragma unroll
-    for (int b = 0; b < kKBatches; ++b) {
-      bf16x8 op[kKB][2];
-      read_k(kvt, b, op);
-      mfma_k(b, op, s0, s1);
+    for (int tl = 1; tl < kAhead && tl < n_tiles; ++tl) {
+      fetch_rows(tl, rid_next);
+      issue_pieces(tl, rid_next, 0, kPiecesMax);
     }
-  };
+    if (n_tiles > kAhead) fetch_rows(kAhead, rid_next);
 
-  // ---- tile loop ----
-  // Iteration j: wait for tile j + 1, barrier (every wave is done with tile
-  // j - 1, whose slot takes tile j + 3), scores of tile j + 1, softmax and
-  // P.V of tile j, with the copies of tile j + 3 spread over the iteration.
-  // Tiles past the end are copied too (their rows all re-read the split's
-  // first row, a few cache lines) and never used: the loop has no branches
-  // around copies, waits or MFMAs, and every wait is the same.
-  f32x4 cur0 = {0.f, 0.f, 0.f, 0.f}, cur1 = cur0;
-  if (n_tiles > 0) {
-    issue_tile(0);
-    issue_tile(1);
-    issue_tile(2);
-    wait_vmcnt<2 * kPiecesPerWave>();
-    __syncthreads();
-    scores(0, cur0, cur1);
-  }
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    wait_vmcnt<kPiecesPerWave>();                        // tile + 1 has landed, tile + 2 may be in flight
-    __syncthreads();
-    int rid[kPiecesPerWave];
-    fetch_rows(tile + 3, rid);
-    issue_pieces(tile + 3, rid, 0, 3);
+    float m_ref = -INFINITY;   // running max (log2 units) of head hl_s
+    float l_part = 0.f;        // this lane's share of that head's denominator
 
-    // The iteration is one software pipeline, fenced so that the compiler
-    // keeps it: operand reads of the next batch are issued before the MFMAs
-    // of the current one, first over the six score batches of tile + 1, then
-    // over the four value batches of tile. The softmax of tile (VALU) runs
-    // while the first score operands are in flight. (The last iteration
-    // scores a stale slot and discards the result.)
-    const uint8_t* kvn = sh.kv[(tile + 1) % kRing];
-    const uint8_t* kvt = sh.kv[tile % kRing];
-    bf16x8 kop[2][kKB][2];
-    i16x4 vlo[2][kVB], vhi[2][kVB];
-    read_k(kvn, 0, kop[0]);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // softmax of tile: lane (c, g) holds head c, rows 4g+i (cur0) and 16+4g+i (cur1)
-    float sv[8];
+    // S[rows, head hl_s] of one tile (lane (c, g): rows 4g + i in s0,
+    // 16 + 4g + i in s1), operands read one batch ahead of their MFMAs.
+    auto scores = [&](const uint8_t* kvt, f32x4& s0, f32x4& s1, int copy_tile, int (&rid)[kPiecesMax]) {
+      auto read_k = [&](int bk, bf16x8 (&dst)[kKB][2]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sv[i] = cur0[i] * scale_log2;
-      sv[4 + i] = cur1[i] * scale_log2;
-    }
-    const int rows_left = nvalid - tile * kMlaTile;      // padding rows (last tile only) -> -inf
+        for (int u = 0; u < kKB; ++u) {
+          const int ks = kKB * bk + u;
+          const int off = ((ks & 1) ? a_off1 : a_off0) + 128 * (ks >> 1);
+          dst[u][0] = *reinterpret_cast<const bf16x8*>(kvt + off);
+          dst[u][1] = *reinterpret_cast<const bf16x8*>(kvt + off + 16 * kRowBytes);
+        }
+      };
+      constexpr int kDepth = kSAhead + 1;
+      bf16x8 op[kDepth][kKB][2];                       // operands read kSAhead batches ahead
+      s0 = f32x4{0.f, 0.f, 0.f, 0.f};
+      s1 = s0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sv[i] = (4 * g + i < rows_left) ? sv[i] : -INFINITY;
-      sv[4 + i] = (16 + 4 * g + i < rows_left) ? sv[4 + i] : -INFINITY;
-    }
-    float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    mx = max_over_groups(mx);
-    float alpha = 1.f;
-    if (mx > m_ref + kRescaleThreshold) {
-      alpha = __builtin_amdgcn_exp2f(m_ref - mx);
-      m_ref = mx;
-      l_part *= alpha;
-    }
-    float pr[8];
+      for (int bk = 0; bk < kSAhead; ++bk) read_k(bk, op[bk]);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pr[i] = __builtin_amdgcn_exp2f(sv[i] - m_ref);
-      l_part += pr[i];
-    }
-    bf16x8 pa;                                           // round to nearest even (v_cvt_pk_bf16_f32)
+      for (int bk = 0; bk < kKBatches; ++bk) {
+        if (bk + kSAhead < kKBatches) read_k(bk + kSAhead, op[(bk + kSAhead) % kDepth]);
+        // this wave's copies early in the interval, for the longest lead
+        if (copy_tile >= 0 && bk < 3) issue_pieces(copy_tile, rid, 2 * bk, min(2 * bk + 2, kPiecesMax));
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bf16x2 two = __builtin_convertvector(f32x2{pr[2 * i], pr[2 * i + 1]}, bf16x2);
-      pa[2 * i] = two[0];
-      pa[2 * i + 1] = two[1];
-    }
-    if (__ballot(alpha != 1.f) != 0ull) {               // rare: rescale O rows (heads 4g + i)
-      float a4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a4[i] = __shfl(alpha, 4 * g + i, kWave);
-#pragma unroll
-      for (int nt = 0; nt < kVTiles; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc_o[nt][i] *= a4[i];
-    }
-
-    // scores of tile + 1
-    f32x4 nxt0 = {0.f, 0.f, 0.f, 0.f}, nxt1 = nxt0;
-#pragma unroll
-    for (int b = 0; b < kKBatches; ++b) {
-      if (b + 1 < kKBatches) read_k(kvn, b + 1, kop[(b + 1) & 1]);
-      else read_v(kvt, 0, vlo[0], vhi[0]);
-      if (b == 1) issue_pieces(tile + 3, rid, 3, 6);
-      if (b == 3) issue_pieces(tile + 3, rid, 6, kPiecesPerWave);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_k(b, kop[b & 1], nxt0, nxt1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // O += P . V(tile)
-#pragma unroll
-    for (int n = 0; n < kVTiles / kVB; ++n) {
-      if (n + 1 < kVTiles / kVB) read_v(kvt, n + 1, vlo[(n + 1) & 1], vhi[(n + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < kVB; ++u) {
-        const i16x8 v8 = __builtin_shufflevector(vlo[n & 1][u], vhi[n & 1][u], 0, 1, 2, 3, 4, 5, 6, 7);
-        acc_o[kVB * n + u] = mfma_bf16(pa, __builtin_bit_cast(bf16x8, v8), acc_o[kVB * n + u]);
+        for (int u = 0; u < kKB; ++u) {
+          s0 = mfma_bf16(op[bk % kDepth][u][0], qf[kKB * bk + u], s0);
+          s1 = mfma_bf16(op[bk % kDepth][u][1], qf[kKB * bk + u], s1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    cur0 = nxt0;
-    cur1 = nxt1;
-  }
-  wait_vmcnt<0>();                                       // no copy into LDS outlives the loop
+    };
+    // online softmax of one tile; returns the bf16 probabilities of the
+    // lane's head at contraction indices 8g .. 8g+7 and its rescale factor
+    auto softmax = [&](int tile, const f32x4& s0, const f32x4& s1, float* alpha) -> bf16x8 {
+      const int rows_left = nvalid - tile * kMlaTile;   // padding rows (last tile only) -> -inf
+      float sv[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[i] = (4 * g + i < rows_left) ? s0[i] * scale_log2 : -INFINITY;
+        sv[4 + i] = (16 + 4 * g + i < rows_left) ? s1[i] * scale_log2 : -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                       fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+      mx = max_over_groups(mx);
+      *alpha = 1.f;
+      if (mx > m_ref + kRescaleThreshold) {
+        *alpha = __builtin_amdgcn_exp2f(m_ref - mx);
+        m_ref = mx;
+        l_part *= *alpha;
+      }
+      float pr[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pr[i] = __builtin_amdgcn_exp2f(sv[i] - m_ref);
+        l_part += pr[i];
+      }
+      bf16x8 pa;                                         // round to nearest even (v_cvt_pk_bf16_f32)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x2 two = __builtin_convertvector(f32x2{pr[2 * i], pr[2 * i + 1]}, bf16x2);
+        pa[2 * i] = two[0];
+        pa[2 * i + 1] = two[1];
+      }
+      return pa;
+    };
+    auto publish = [&](const bf16x8& pa, float alpha) {  // between B1 and B2
+      *reinterpret_cast<bf16x8*>(&sh.p[hl_s * kMlaTile + 8 * g]) = pa;
+      if (g == 0) sh.alpha[hl_s] = alpha;
+      const bool any = __ballot(alpha != 1.f) != 0ull;
+      if (lane == 0) sh.flag[rw] = any ? 1 : 0;
+    };
 
-  // ---- finish: denominators, lse, normalized output ----
-  const float l = sum_over_groups(l_part);               // head c
-  if (g == 0) {
-    const float lse_val = (l > 0.f) ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
-    if (S == 1) {
-      if (p.lse) p.lse[(int64_t)t * Hm + head0 + c] = lse_val;
-    } else {
-      p.part_lse[((int64_t)t * S + s) * Hm + head0 + c] = lse_val;
+    if (n_tiles > 0) {                                 // prologue: tile 0
+      wait_tiles(min(n_tiles, kAhead) - 1, five);      // tile 0 has landed
+      __syncthreads();
+      f32x4 s0, s1;
+      scores(sh.kv[0], s0, s1, -1, rid_next);
+      float alpha;
+      const bf16x8 pa = softmax(0, s0, s1, &alpha);
+      publish(pa, alpha);
+      wait_tiles(min(n_tiles, kAhead) - 2, five);      // tile 1 has landed
+      __syncthreads();
     }
-  }
-  float inv[4];
+    for (int tile = 0; tile < n_tiles; ++tile) {
+      const bool more = tile + 1 < n_tiles;            // uniform
+      bf16x8 pa;
+      float alpha = 1.f;
+      const int last = n_tiles - 1;
+      const int copy_tile = tile + kAhead <= last ? tile + kAhead : -1;   // uniform
+      if (more) {
+        f32x4 s0, s1;
+        scores(sh.kv[(tile + 1) % kRing], s0, s1, copy_tile, rid_next);
+        pa = softmax(tile + 1, s0, s1, &alpha);
+      } else if (copy_tile >= 0) {
+        issue_pieces(copy_tile, rid_next, 0, kPiecesMax);
+      }
+      if (copy_tile >= 0 && copy_tile + 1 <= last) fetch_rows(copy_tile + 1, rid_next);
+      __syncthreads();                                 // B1: every value wave holds P of tile
+      if (more) publish(pa, alpha);
+      wait_tiles(min(tile + kAhead, last) - (tile + 2), five);   // tile + 2 has landed
+      __syncthreads();                                 // B2
+    }
+    // denominators, lse; 1 / l for the value waves
+    const float l = sum_over_groups(l_part);
+    if (g == 0) {
+      const float lse_val = (l > 0.f) ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
+      if (S == 1) {
+        if (p.lse) p.lse[(int64_t)t * Hm + hbase + hl_s] = lse_val;
+      } else {
+        p.part_lse[((int64_t)t * S + s) * Hm + hbase + hl_s] = lse_val;
+      }
+      sh.alpha[hl_s] = l > 0.f ? 1.f / l : 0.f;
+    }
+    __syncthreads();
+  } else {
+    // ================= value waves =================
+    for (int tl = 0; tl < kAhead && tl < n_tiles; ++tl) {
+      fetch_rows(tl, rid_next);
+      issue_pieces(tl, rid_next, 0, kPiecesMax);
+    }
+    if (n_tiles > kAhead) fetch_rows(kAhead, rid_next);
+    f32x4 acc_o[kPvHT][kPvNT];   // O[head 16 hb + c][value column 128 v + 16 nt + 4g + i]
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float li = __shfl(l, 4 * g + i, kWave);        // head 4g + i
-    inv[i] = li > 0.f ? 1.f / li : 0.f;
-  }
+    for (int hb = 0; hb < kPvHT; ++hb)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = head0 + 4 * g + i;
-    if (S == 1) {
-      uint16_t* orow = static_cast<uint16_t*>(p.out) + ((int64_t)t * Hm + h) * kMlaDl;
+      for (int nt = 0; nt < kPvNT; ++nt) acc_o[hb][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (n_tiles > 0) {                                 // prologue (score waves: tile 0)
+      wait_tiles(min(n_tiles, kAhead) - 1, five);      // tile 0 has landed
+      __syncthreads();
+      wait_tiles(min(n_tiles, kAhead) - 2, five);      // tile 1 has landed
+      __syncthreads();
+    }
+    for (int tile = 0; tile < n_tiles; ++tile) {
+      const uint8_t* kvt = sh.kv[tile % kRing];
+      const int last = n_tiles - 1;
+      const int copy_tile = tile + kAhead <= last ? tile + kAhead : -1;   // uniform
+      // P of this tile; (rare) the heads whose running max moved with this
+      // tile rescale their O first
+      const i32x4 fl4 = *reinterpret_cast<const i32x4*>(sh.flag);
+      bf16x8 pb[kPvHT];
 #pragma unroll
-      for (int nt = 0; nt < kVTiles; ++nt) orow[16 * nt + c] = f32_to_bf16_bits(acc_o[nt][i] * inv[i]);
-    } else {
-      float* orow = p.part_o + (((int64_t)t * S + s) * Hm + h) * kMlaDl;
+      for (int hb = 0; hb < kPvHT; ++hb)
+        pb[hb] = *reinterpret_cast<const bf16x8*>(&sh.p[16 * hb * kMlaTile + p_off]);
+      if (__builtin_amdgcn_readfirstlane(fl4[0] | fl4[1] | fl4[2] | fl4[3])) {
 #pragma unroll
-      for (int nt = 0; nt < kVTiles; ++nt) orow[16 * nt + c] = acc_o[nt][i] * inv[i];
+        for (int hb = 0; hb < kPvHT; ++hb) {
+          const float a = sh.alpha[16 * hb + c];
+#pragma unroll
+          for (int nt = 0; nt < kPvNT; ++nt) acc_o[hb][nt] *= a;
+        }
+      }
+      // O += P . V(tile), value operands read kVAhead column tiles ahead of their MFMAs
+      i16x4 vlo[kVAhead], vhi[kVAhead];
+      auto read_v = [&](int nt) {
+        const int imm = 128 * (nt >> 2);
+        vlo[nt % kVAhead] = lds_read_tr16(kvt + v_off[0][nt & 3] + imm);
+        vhi[nt % kVAhead] = lds_read_tr16(kvt + v_off[1][nt & 3] + imm);
+      };
+#pragma unroll
+      for (int nt = 0; nt < kVAhead; ++nt) read_v(nt);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nt = 0; nt < kPvNT; ++nt) {
+        const bf16x8 v8 = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(vlo[nt % kVAhead], vhi[nt % kVAhead], 0, 1, 2, 3, 4, 5, 6, 7));
+        if (nt + kVAhead < kPvNT) read_v(nt + kVAhead);
+        if (copy_tile >= 0 && nt < 2) issue_pieces(copy_tile, rid_next, 2 * nt, 2 * nt + 2);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int hb = 0; hb < kPvHT; ++hb) acc_o[hb][nt] = mfma_bf16(v8, pb[hb], acc_o[hb][nt]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (copy_tile >= 0 && copy_tile + 1 <= last) fetch_rows(copy_tile + 1, rid_next);
+      __syncthreads();                                 // B1: done with tile's slot
+      wait_tiles(min(tile + kAhead, last) - (tile + 2), five);   // tile + 2 has landed
+      __syncthreads();                                 // B2
+    }
+    __syncthreads();                                   // 1 / l of every head is in LDS
+#pragma unroll
+    for (int hb = 0; hb < kPvHT; ++hb) {
+      const float inv = sh.alpha[16 * hb + c];
+      const int h = hbase + 16 * hb + c;
+      const int col0 = 128 * rw + 4 * g;
+      if (S == 1) {
+        uint16_t* orow = static_cast<uint16_t*>(p.out) + ((int64_t)t * Hm + h) * kMlaDl + col0;
+#pragma unroll
+        for (int nt = 0; nt < kPvNT; ++nt) {
+          const f32x4 o = acc_o[hb][nt] * inv;
+          *reinterpret_cast<bf16x4*>(orow + 16 * nt) = __builtin_convertvector(o, bf16x4);
+        }
+      } else {
+        float* orow = p.part_o + (((int64_t)t * S + s) * Hm + h) * kMlaDl + col0;
+#pragma unroll
+        for (int nt = 0; nt < kPvNT; ++nt) *reinterpret_cast<f32x4*>(orow + 16 * nt) = acc_o[hb][nt] * inv;
+      }
     }
   }
 }
