@@ -4,38 +4,39 @@
 // forward_indexer takes topk(min(topk, seq_len)) and pads with -1;
 // _forward_cuda_k_only relies on rows of length <= k giving [0 .. len-1, -1 ...].)
 //
-// One work-group of 512 threads per row. Scores become order-preserving 32-bit
+// One work-group of 1024 threads per row (four waves per SIMD, so that the
+// latency of one wave's LDS and memory operations is covered by the others). Scores become order-preserving 32-bit
 // keys. A radix select on the key bits (12 + 12 + 8 bits, three LDS histograms)
 // finds the exact k-th largest key `thr` and how many of the k winners are equal
 // to it. A last ordered pass writes the winners in ascending position order:
 // everything above `thr`, plus the first `need` positions equal to `thr`, so ties
 // go to the lower positions.
 //
-// Rows of up to 32768 scores are read from HBM once: each thread keeps sixteen
+// Rows of up to 32768 scores are read from HBM once: each thread keeps eight
 // 16-byte loads in flight (the whole row is requested at once), converts them to
 // keys into LDS and counts the first digit on the way. Longer rows are re-read
 // from global memory (L2) by each pass. The histogram passes handle 8
 // consecutive positions per thread per step; keys sharing the first digit with
 // the k-th largest are appended (wave-aggregated) to a candidate list for the
 // last digit. The ordered output gives each thread one contiguous run of
-// positions: count winners in the run, one block-wide scan, write the run's
-// winners in order.
+// positions: count winners in the run, one block-wide scan, place the run's
+// winners in order in LDS, then write the row out with coalesced stores.
 #include "device_common.h"
 #include "dsa_internal.h"
 
 namespace dsa {
 namespace {
 
-constexpr int kTkThreads = 512;
+constexpr int kTkThreads = 1024;
 constexpr int kTkWaves = kTkThreads / kWave;
 constexpr int kTkCache = 32768;
 constexpr int kTkBins = 4096;
-constexpr int kTkLoadUnroll = 16;          // float4 loads in flight per thread
+constexpr int kTkLoadUnroll = 8;           // float4 loads in flight per thread
 constexpr int kTkPer = 8;                  // consecutive positions per thread per pass step
 constexpr int kTkCand = 4032;              // keys sharing the top 12 bits kept for the last level
-constexpr int kTkRun = kTkCache / kTkThreads;   // 64 positions per thread in the output pass (cached rows)
-constexpr int kTkCandPerWave = kTkCand / kTkWaves; // 504 candidate slots per wave
-static_assert(kTkRun == 64, "the output pass handles one 64-position mask per cached run");
+constexpr int kTkRun = kTkCache / kTkThreads;   // 32 positions per thread in the output pass (cached rows)
+constexpr int kTkCandPerWave = kTkCand / kTkWaves; // 252 candidate slots per wave
+static_assert(kTkRun == 32, "the output pass handles one 32-position mask per cached run");
 
 struct TopkShared {
   uint32_t hist[kTkBins];
@@ -48,12 +49,13 @@ struct TopkShared {
   uint32_t sel_above;
 };
 
-// LDS word of position p. Each run of 64 positions (one thread's run in the
-// output pass) keeps its sixteen 16-byte blocks, block j stored at j ^ (run % 16),
-// so that consecutive threads reading their runs block by block, and
-// consecutive threads reading consecutive blocks, hit distinct banks.
+// LDS word of position p. Each run of 32 positions (one thread's run in the
+// output pass) keeps its eight 16-byte blocks, block j of run r stored at
+// j ^ ((r >> 1) % 8), so that consecutive threads reading their runs block by
+// block, and consecutive threads reading consecutive blocks, spread over the
+// banks.
 __device__ __forceinline__ int kslot(int p) {
-  return (p & ~63) | ((((p >> 2) & 15) ^ ((p >> 6) & 15)) << 2) | (p & 3);
+  return (p & ~31) | ((((p >> 2) & 7) ^ ((p >> 6) & 7)) << 2) | (p & 3);
 }
 
 // Keys of positions [i, i + 8) (i a multiple of 8); positions >= n give 0.
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
   for (int i = tid; i < kTkBins; i += kTkThreads) sh.hist[i] = 0;
   if (tid == 0) sh.n_cand = 0;
   __syncthreads();
-  // Each wave appends its matches to its own 504 slots of the list (ballot and
+  // Each wave appends its matches to its own 252 slots of the list (ballot and
   // lane rank: no returning atomics in the loop); a wave that runs out of
   // slots makes the last digit take the full pass instead.
   const int wave = wave_id();
@@ -264,51 +266,49 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
   // ---- ordered output ----
   // A winner at position p goes to slot #winners before p = (#keys > thr before
   // p) + min(#keys == thr before p, need). Thread tid owns a run of
-  // consecutive positions, handled 64 at a time as bit masks: count its winners,
-  // one block-wide scan, then write them in order.
-  const int run_len = cached ? kTkRun : ((n + kTkThreads - 1) / kTkThreads + 63) & ~63;
+  // consecutive positions, handled 32 at a time as bit masks: count its winners,
+  // one block-wide scan, then place them in order.
+  const int run_len = cached ? kTkRun : ((n + kTkThreads - 1) / kTkThreads + 31) & ~31;
   const int run0 = run_len * tid;
-  // masks of the keys > thr and == thr among positions [p0, p0 + 64)
-  auto masks64 = [&](int p0, uint64_t* gtm, uint64_t* eqm) {
-    uint32_t key[64];
+  // masks of the keys > thr and == thr among positions [p0, p0 + 32)
+  auto masks32 = [&](int p0, uint32_t* gtm, uint32_t* eqm) {
+    uint32_t key[32];
     if (cached) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
+      for (int j = 0; j < 8; ++j) {
         const i32x4 a = *reinterpret_cast<const i32x4*>(sh.keys + kslot(p0 + 4 * j));
 #pragma unroll
         for (int e = 0; e < 4; ++e) key[4 * j + e] = (uint32_t)a[e];
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 4; ++j) {
         uint32_t u[kTkPer];
         load8(row, sh, false, n, p0 + 8 * j, u);
 #pragma unroll
         for (int e = 0; e < kTkPer; ++e) key[8 * j + e] = u[e];
       }
     }
-    uint32_t g0 = 0, g1 = 0, q0 = 0, q1 = 0;
+    uint32_t g = 0, q = 0;
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
-      g0 |= (key[e] > thr ? 1u : 0u) << e;
-      q0 |= (key[e] == thr ? 1u : 0u) << e;
-      g1 |= (key[32 + e] > thr ? 1u : 0u) << e;
-      q1 |= (key[32 + e] == thr ? 1u : 0u) << e;
+      g |= (key[e] > thr ? 1u : 0u) << e;
+      q |= (key[e] == thr ? 1u : 0u) << e;
     }
     const int nv = n - p0;                                  // valid positions in the block
-    const uint64_t vmask = nv >= 64 ? ~0ull : (nv <= 0 ? 0ull : ((1ull << nv) - 1ull));
-    *gtm = (((uint64_t)g1 << 32) | g0) & vmask;
-    *eqm = (((uint64_t)q1 << 32) | q0) & vmask;
+    const uint32_t vmask = nv >= 32 ? ~0u : (nv <= 0 ? 0u : ((1u << nv) - 1u));
+    *gtm = g & vmask;
+    *eqm = q & vmask;
   };
   uint32_t cgt = 0, ceq = 0;
-  uint64_t gtm0 = 0, eqm0 = 0;                          // cached rows: the run's only block, kept for the write
-  for (int p0 = run0; p0 < run0 + run_len && p0 < n; p0 += 64) {
-    uint64_t gtm, eqm;
-    masks64(p0, &gtm, &eqm);
+  uint32_t gtm0 = 0, eqm0 = 0;                          // cached rows: the run's only block, kept for the write
+  for (int p0 = run0; p0 < run0 + run_len && p0 < n; p0 += 32) {
+    uint32_t gtm, eqm;
+    masks32(p0, &gtm, &eqm);
     gtm0 = gtm;
     eqm0 = eqm;
-    cgt += (uint32_t)__builtin_popcountll(gtm);
-    ceq += (uint32_t)__builtin_popcountll(eqm);
+    cgt += (uint32_t)__builtin_popcount(gtm);
+    ceq += (uint32_t)__builtin_popcount(eqm);
   }
   uint32_t total_gt, total_eq;
   const uint32_t gt_incl = block_scan(sh, cgt, 1, &total_gt);
@@ -316,25 +316,30 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
   uint32_t eq_before = eq_incl - ceq;
   uint32_t slot = (gt_incl - cgt) + (eq_before < need ? eq_before : need);
   if (cgt + ceq) {
-    for (int p0 = run0; p0 < run0 + run_len && p0 < n; p0 += 64) {
-      uint64_t gtm = gtm0, eqm = eqm0;
-      if (!cached) masks64(p0, &gtm, &eqm);
+    for (int p0 = run0; p0 < run0 + run_len && p0 < n; p0 += 32) {
+      uint32_t gtm = gtm0, eqm = eqm0;
+      if (!cached) masks32(p0, &gtm, &eqm);
       // the first (need - eq_before) ties of the block are winners
-      uint64_t win = gtm;
+      uint32_t win = gtm;
       for (uint32_t r = eq_before; r < need && eqm; ++r) {
-        const uint64_t low = eqm & (0ull - eqm);
+        const uint32_t low = eqm & (0u - eqm);
         win |= low;
         eqm ^= low;
       }
-      eq_before += (uint32_t)__builtin_popcountll(eqm) + (uint32_t)__builtin_popcountll(win & ~gtm);
+      eq_before += (uint32_t)__builtin_popcount(eqm) + (uint32_t)__builtin_popcount(win & ~gtm);
       while (win) {
-        const int e = __builtin_ctzll(win);
-        if (slot < (uint32_t)k) out[slot] = p0 + e;
+        const int e = __builtin_ctz(win);
+        if (slot < (uint32_t)k) sh.keys[slot] = (uint32_t)(p0 + e);
         ++slot;
-        win &= win - 1ull;
+        win &= win - 1u;
       }
     }
   }
+  // The winners were staged in LDS (the key area is free once every thread
+  // has its masks, i.e. after the scans' barriers); the row leaves in
+  // consecutive, coalesced stores instead of each thread's scattered ones.
+  __syncthreads();
+  for (int i = tid; i < k; i += kTkThreads) out[i] = (int32_t)sh.keys[i];
 }
 
 }  // namespace
