@@ -100,7 +100,8 @@ dsa_status_t plan_mla(const BatchView& bv, int32_t k, int32_t num_heads, int32_t
     plan->workspace = 0;
     if (plan->splits > 1) {
       const size_t parts = (size_t)bv.num_rows * plan->splits * num_heads;
-      plan->workspace = parts * (size_t)d_latent * sizeof(float) + parts * sizeof(float);
+      // partial outputs in bf16, then their fp32 log-sum-exps
+      plan->workspace = parts * (size_t)d_latent * sizeof(uint16_t) + parts * sizeof(float);
     }
     return ok();
   }
@@ -159,8 +160,8 @@ dsa_status_t run_mla(const dsa_batch_t* batch, bool decode, const void* q, const
   p.part_lse = nullptr;
   if (plan.splits > 1) {
     const size_t parts = (size_t)bv.num_rows * plan.splits * num_heads;
-    p.part_o = static_cast<float*>(workspace);
-    p.part_lse = static_cast<float*>(workspace) + parts * (size_t)d_latent;
+    p.part_o = static_cast<uint16_t*>(workspace);
+    p.part_lse = reinterpret_cast<float*>(static_cast<uint16_t*>(workspace) + parts * (size_t)d_latent);
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   return from_hip(plan.bf16 ? launch_mla_bf16(p, s) : launch_mla_f32(p, s), "sparse MLA launch");

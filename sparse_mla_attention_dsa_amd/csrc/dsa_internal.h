@@ -52,8 +52,9 @@ struct MlaParams {
   float softmax_scale;
   void* out;              // [T, Hm, Dl]
   float* lse;             // [T, Hm] or nullptr
-  // split-KV partials (splits > 1): [T, splits, Hm, Dl] fp32 and [T, splits, Hm]
-  float* part_o;
+  // split-KV partials (splits > 1): O / l as [T, splits, Hm, Dl] bf16 bits and
+  // the lse as [T, splits, Hm] fp32
+  uint16_t* part_o;
   float* part_lse;
   int32_t splits;
   int32_t entries_per_split;  // multiple of the tile height

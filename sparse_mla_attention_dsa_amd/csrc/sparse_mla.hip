@@ -40,8 +40,8 @@
 // barrier B1; the score waves write P of tile j+1; every wave waits for its
 // copies of tile j+2; barrier B2.
 //
-// Single split: out = O / l in bf16 and lse; several splits: fp32 partials
-// (O / l, lse) merged by mla_combine_kernel. Work-groups are ordered so that
+// Single split: out = O / l in bf16 and lse; several splits: partials (O / l
+// in bf16, lse in fp32) merged by mla_combine_kernel in fp32. Work-groups are ordered so that
 // the head groups of one (row, split) unit, and neighbouring units, land on
 // the same XCD (work-group i runs on XCD i % 8) and share the gathered rows
 // through that XCD's L2.
@@ -496,9 +496,12 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
           *reinterpret_cast<bf16x4*>(orow + 16 * nt) = __builtin_convertvector(o, bf16x4);
         }
       } else {
-        float* orow = p.part_o + (((int64_t)t * S + s) * Hm + h) * kMlaDl + col0;
+        uint16_t* orow = p.part_o + (((int64_t)t * S + s) * Hm + h) * kMlaDl + col0;
 #pragma unroll
-        for (int nt = 0; nt < kPvNT; ++nt) *reinterpret_cast<f32x4*>(orow + 16 * nt) = acc_o[hb][nt] * inv;
+        for (int nt = 0; nt < kPvNT; ++nt) {
+          const f32x4 o = acc_o[hb][nt] * inv;
+          *reinterpret_cast<bf16x4*>(orow + 16 * nt) = __builtin_convertvector(o, bf16x4);
+        }
       }
     }
   }
@@ -522,7 +525,8 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaParams p) {
     const float l = pl[(int64_t)s * Hm];
     const float wgt = (l == -INFINITY) ? 0.f : __expf(l - mx);
     tot += wgt;
-    const f32x4 o = *reinterpret_cast<const f32x4*>(p.part_o + (((int64_t)t * S + s) * Hm + h) * Dl + 4 * d4);
+    const bf16x4 ob = *reinterpret_cast<const bf16x4*>(p.part_o + (((int64_t)t * S + s) * Hm + h) * Dl + 4 * d4);
+    const f32x4 o = __builtin_convertvector(ob, f32x4);
     acc += wgt * o;
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;

@@ -133,7 +133,9 @@ def _mla(L, batch, decode=True, dtype=dsa.DSA_BF16, H=128, Dl=512, Dr=64, k=2048
 def test_mla_validation(L):
     dec = _batch(num_seqs=64, num_rows=64)
     need = L.dsa_workspace_bytes(dsa.DSA_OP_MLA_DECODE, ctypes.byref(dec), 2048, 128, 512, dsa.DSA_BF16)
-    assert need > 0                                         # split-KV partials for a 64-row decode
+    # split-KV partials for a 64-row decode: 2 splits x 128 heads per row, a bf16
+    # O / l of 512 values and an fp32 lse each
+    assert need == 64 * 2 * 128 * (512 * 2 + 4)
     assert _mla(L, dec, ws=None, wsb=0) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
     assert _mla(L, dec, ws=None, wsb=need) == dsa.DSA_ERR_INVALID_ARGUMENT
     assert _mla(L, dec, H=96, ws=ctypes.c_void_p(0x50), wsb=need) == dsa.DSA_ERR_UNSUPPORTED
