@@ -133,7 +133,10 @@ dsa_status_t dsa_indexer_logits(const dsa_batch_t *batch,
  *           positions are taken. Values are compared as floats with -0 == +0;
  *           logits must not be NaN.
  * topk_idx: [T, k] int32 logical positions. 1 <= k <= 4096.
- * workspace: dsa_workspace_bytes(DSA_OP_TOPK, ...) bytes (currently 0; NULL ok).
+ * workspace: at least dsa_workspace_bytes(DSA_OP_TOPK, ...) bytes of device
+ *           memory, else DSA_ERR_WORKSPACE_TOO_SMALL. It is non-zero for batches
+ *           of few, long rows, which are selected in two phases (per chunk of
+ *           the row, then among the chunks' candidates); NULL if it is 0.
  */
 dsa_status_t dsa_topk(const dsa_batch_t *batch,
                       const float *logits, int64_t logits_row_stride, int32_t k,

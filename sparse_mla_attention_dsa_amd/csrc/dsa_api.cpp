@@ -217,8 +217,6 @@ dsa_status_t dsa_indexer_logits(const dsa_batch_t* batch, const void* q, dsa_dty
 dsa_status_t dsa_topk(const dsa_batch_t* batch, const float* logits, int64_t logits_row_stride,
                       int32_t k, int32_t* topk_idx, void* workspace, size_t workspace_bytes,
                       dsa_stream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   BatchView bv;
   dsa_status_t st = check_batch(batch, &bv);
   if (st != DSA_OK) return st;
@@ -226,6 +224,10 @@ dsa_status_t dsa_topk(const dsa_batch_t* batch, const float* logits, int64_t log
   if (logits_row_stride < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "logits_row_stride < 1");
   if (bv.num_rows > 0 && (!logits || !topk_idx))
     return fail(DSA_ERR_INVALID_ARGUMENT, "logits / topk_idx is NULL");
+  const size_t need = topk_workspace_bytes(bv.num_rows, bv.max_seq_len_k, k);
+  if (workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  if (need > 0 && !workspace) return fail(DSA_ERR_INVALID_ARGUMENT, "workspace is NULL");
   if (bv.num_rows == 0) return ok();
   TopkParams p;
   p.batch = bv;
@@ -233,6 +235,11 @@ dsa_status_t dsa_topk(const dsa_batch_t* batch, const float* logits, int64_t log
   p.stride = logits_row_stride;
   p.k = k;
   p.topk_idx = topk_idx;
+  p.chunk = need > 0 ? topk_chunk(bv.num_rows, bv.max_seq_len_k, k) : 0;
+  p.chunks = p.chunk > 0 ? (bv.max_seq_len_k + p.chunk - 1) / p.chunk : 0;
+  const size_t cands = (size_t)bv.num_rows * p.chunks * k;
+  p.cand_key = p.chunk > 0 ? static_cast<uint32_t*>(workspace) : nullptr;
+  p.cand_pos = p.chunk > 0 ? reinterpret_cast<int32_t*>(static_cast<uint32_t*>(workspace) + cands) : nullptr;
   return from_hip(launch_topk(p, reinterpret_cast<hipStream_t>(stream)), "top-k launch");
 }
 
@@ -263,7 +270,7 @@ size_t dsa_workspace_bytes(dsa_op_t op, const dsa_batch_t* batch, int32_t k, int
       fail(DSA_ERR_INVALID_ARGUMENT, "k %d outside [1, %d]", k, kTopkMaxK);
       return (size_t)-1;
     }
-    return 0;
+    return topk_workspace_bytes(bv.num_rows, bv.max_seq_len_k, k);
   }
   if (op == DSA_OP_MLA_DECODE || op == DSA_OP_MLA_PREFILL) {
     MlaPlan plan;

@@ -38,6 +38,11 @@ struct TopkParams {
   int64_t stride;
   int32_t k;
   int32_t* topk_idx;      // [T, k]
+  // two phases (chunk > 0): per (row, chunk) candidates [T, chunks, k]
+  int32_t chunk;          // positions per chunk, 0 = one work-group per row
+  int32_t chunks;         // chunks of the longest row
+  uint32_t* cand_key;     // order-preserving keys
+  int32_t* cand_pos;      // positions
 };
 
 struct MlaParams {
@@ -75,6 +80,11 @@ constexpr int kTopkMaxK = 4096;
 // while keeping every split at least a few tiles long.
 int mla_bf16_splits(int num_rows, int k, int heads);
 int mla_entries_per_split(int k, int splits);
+
+// Top-k plan: chunk length of the two-phase selection (0 = one phase) and the
+// workspace it needs.
+int topk_chunk(int num_rows, int max_len, int k);
+size_t topk_workspace_bytes(int num_rows, int max_len, int k);
 
 hipError_t launch_indexer_fp8(const IndexerParams& p, hipStream_t s);
 hipError_t launch_indexer_f32(const IndexerParams& p, hipStream_t s);

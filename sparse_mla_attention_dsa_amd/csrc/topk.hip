@@ -4,8 +4,15 @@
 // forward_indexer takes topk(min(topk, seq_len)) and pads with -1;
 // _forward_cuda_k_only relies on rows of length <= k giving [0 .. len-1, -1 ...].)
 //
-// One work-group of 1024 threads per row (four waves per SIMD, so that the
-// latency of one wave's LDS and memory operations is covered by the others). Scores become order-preserving 32-bit
+// One work-group of 1024 threads per selection (four waves per SIMD, so that
+// the latency of one wave's LDS and memory operations is covered by the
+// others). A selection is a whole row when there are enough rows to fill the
+// chip. Otherwise (few rows, long rows) the row is cut into chunks: phase one
+// selects, per (row, chunk), the chunk's own top k (key, position) pairs into
+// the workspace, in position order; phase two selects the row's top k among
+// the concatenated candidates. This is exact: an element of the row's top k
+// has fewer than k elements before it in (key descending, position ascending)
+// order within its own chunk, so its chunk keeps it. Scores become order-preserving 32-bit
 // keys. A radix select on the key bits (12 + 12 + 8 bits, three LDS histograms)
 // finds the exact k-th largest key `thr` and how many of the k winners are equal
 // to it. A last ordered pass writes the winners in ascending position order:
@@ -58,8 +65,16 @@ __device__ __forceinline__ int kslot(int p) {
   return (p & ~31) | ((((p >> 2) & 7) ^ ((p >> 6) & 7)) << 2) | (p & 3);
 }
 
-// Keys of positions [i, i + 8) (i a multiple of 8); positions >= n give 0.
-__device__ __forceinline__ void load8(const float* __restrict__ row, const TopkShared& sh, bool cached,
+// Key of element q of a selection's source: a logit (converted) or a candidate key.
+template <bool kKeys>
+__device__ __forceinline__ uint32_t src_key(const void* __restrict__ src, int q) {
+  if (kKeys) return static_cast<const uint32_t*>(src)[q];
+  return ordered_key(static_cast<const float*>(src)[q]);
+}
+
+// Keys of elements [i, i + 8) (i a multiple of 8); elements >= n give 0.
+template <bool kKeys>
+__device__ __forceinline__ void load8(const void* __restrict__ src, const TopkShared& sh, bool cached,
                                       int n, int i, uint32_t (&u)[kTkPer]) {
   if (cached) {
     const i32x4 a = *reinterpret_cast<const i32x4*>(sh.keys + kslot(i));
@@ -70,7 +85,7 @@ __device__ __forceinline__ void load8(const float* __restrict__ row, const TopkS
 #pragma unroll
     for (int e = 0; e < kTkPer; ++e) {
       const int q = i + e < n ? i + e : n - 1;   // clamped: always in bounds
-      u[e] = ordered_key(row[q]);
+      u[e] = src_key<kKeys>(src, q);
     }
   }
 #pragma unroll
@@ -132,7 +147,11 @@ __device__ void select_bin(TopkShared& sh, int nbins, uint32_t need, int buf, ui
   *above = sh.sel_above;
 }
 
+enum TopkMode { kWholeRow = 0, kChunk = 1, kMerge = 2 };
+
+template <int kMode>
 __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
+  constexpr bool kKeys = kMode == kMerge;             // the source holds keys, not logits
   __shared__ TopkShared sh;
   const BatchView& bv = p.batch;
   const int t = blockIdx.x;
@@ -142,39 +161,64 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
   int cap = bv.max_pages_per_seq * bv.page_size;
   if (cap > bv.max_seq_len_k) cap = bv.max_seq_len_k;
   if ((int64_t)cap > p.stride) cap = (int)p.stride;
-  const int n = visible_keys(bv.seq_lens_k[b], q_len, j, cap);
+  const int n_row = visible_keys(bv.seq_lens_k[b], q_len, j, cap);
   const int k = p.k;
   int32_t* out = p.topk_idx + (int64_t)t * k;
+  const int64_t cand0 = ((int64_t)t * p.chunks + (kMode == kChunk ? blockIdx.y : 0)) * k;
 
-  if (n <= k) {  // short row: every visible position, in order, then -1
-    for (int i = tid; i < k; i += kTkThreads) out[i] = i < n ? i : -1;
+  // this selection: elements [0, n) of `src`
+  int n = n_row;
+  int base = 0;                                       // chunk: position of element 0
+  const void* src = p.logits + (int64_t)t * p.stride;
+  if (kMode == kChunk) {
+    if (n_row <= k) return;                           // short rows are the merge's
+    base = (int)blockIdx.y * p.chunk;
+    if (base >= n_row) return;
+    n = min(p.chunk, n_row - base);
+    src = p.logits + (int64_t)t * p.stride + base;
+    if (n <= k) {                                     // the whole chunk is a candidate
+      for (int i = tid; i < n; i += kTkThreads) {
+        p.cand_key[cand0 + i] = src_key<false>(src, i);
+        p.cand_pos[cand0 + i] = base + i;
+      }
+      return;
+    }
+  } else if (kMode == kMerge) {
+    if (n_row > k) {                                  // every chunk but the last gave k candidates
+      const int nch = (n_row + p.chunk - 1) / p.chunk;
+      n = (nch - 1) * k + min(k, n_row - (nch - 1) * p.chunk);
+    }
+    src = p.cand_key + cand0;
+  }
+  if (n <= k) {  // short row (or as many candidates as winners): every element, in order, then -1
+    for (int i = tid; i < k; i += kTkThreads)
+      out[i] = i < n ? (kMode == kMerge && n_row > k ? p.cand_pos[cand0 + i] : i) : -1;
     return;
   }
 
-  const float* row = p.logits + (int64_t)t * p.stride;
   const bool cached = n <= kTkCache;
   for (int i = tid; i < kTkBins; i += kTkThreads) sh.hist[i] = 0;
   __syncthreads();
 
   // ---- level 0 (bits 31..20) while reading the row once ----
-  const bool vec = ((reinterpret_cast<uintptr_t>(row) & 15u) == 0);
+  const bool vec = ((reinterpret_cast<uintptr_t>(src) & 15u) == 0);
   const int n4 = vec ? n / 4 : 0;
-  for (int base = 0; base < n4; base += kTkThreads * kTkLoadUnroll) {
-    f32x4 v[kTkLoadUnroll];
+  for (int i0 = 0; i0 < n4; i0 += kTkThreads * kTkLoadUnroll) {
+    i32x4 v[kTkLoadUnroll];
 #pragma unroll
     for (int u = 0; u < kTkLoadUnroll; ++u) {
-      int i4 = base + u * kTkThreads + tid;
+      int i4 = i0 + u * kTkThreads + tid;
       i4 = i4 < n4 ? i4 : n4 - 1;               // clamped: always in bounds
-      v[u] = reinterpret_cast<const f32x4*>(row)[i4];
+      v[u] = static_cast<const i32x4*>(src)[i4];
     }
 #pragma unroll
     for (int u = 0; u < kTkLoadUnroll; ++u) {
-      const int i4 = base + u * kTkThreads + tid;
+      const int i4 = i0 + u * kTkThreads + tid;
       if (i4 < n4) {
         uint32_t kk[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          kk[e] = ordered_key(v[u][e]);
+          kk[e] = kKeys ? (uint32_t)v[u][e] : ordered_key(__int_as_float(v[u][e]));
           atomicAdd(&sh.hist[kk[e] >> 20], 1u);
         }
         if (cached)
@@ -183,7 +227,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
     }
   }
   for (int i = 4 * n4 + tid; i < n; i += kTkThreads) {
-    const uint32_t kk = ordered_key(row[i]);
+    const uint32_t kk = src_key<kKeys>(src, i);
     if (cached) sh.keys[kslot(i)] = kk;
     atomicAdd(&sh.hist[kk >> 20], 1u);
   }
@@ -208,7 +252,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
   uint32_t wcnt = 0;                                   // this wave's matches so far (wave-uniform)
   for (int i = kTkPer * tid; i < n; i += kTkPer * kTkThreads) {
     uint32_t u[kTkPer];
-    load8(row, sh, cached, n, i, u);
+    load8<kKeys>(src, sh, cached, n, i, u);
     // matches are rare: each round handles one match per lane, so a wave issues
     // as many LDS atomics as its busiest lane has matches (not one per element)
     uint32_t mm = 0;
@@ -252,7 +296,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
   } else {
     for (int i = kTkPer * tid; i < n; i += kTkPer * kTkThreads) {
       uint32_t u[kTkPer];
-      load8(row, sh, cached, n, i, u);
+      load8<kKeys>(src, sh, cached, n, i, u);
 #pragma unroll
       for (int e = 0; e < kTkPer; ++e)
         if (i + e < n && (u[e] >> 8) == prefix) atomicAdd(&sh.hist[u[e] & 0xffu], 1u);
@@ -284,7 +328,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         uint32_t u[kTkPer];
-        load8(row, sh, false, n, p0 + 8 * j, u);
+        load8<kKeys>(src, sh, false, n, p0 + 8 * j, u);
 #pragma unroll
         for (int e = 0; e < kTkPer; ++e) key[8 * j + e] = u[e];
       }
@@ -329,24 +373,63 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
       eq_before += (uint32_t)__builtin_popcount(eqm) + (uint32_t)__builtin_popcount(win & ~gtm);
       while (win) {
         const int e = __builtin_ctz(win);
-        if (slot < (uint32_t)k) sh.keys[slot] = (uint32_t)(p0 + e);
+        if (slot < (uint32_t)k) sh.hist[slot] = (uint32_t)(p0 + e);
         ++slot;
         win &= win - 1u;
       }
     }
   }
-  // The winners were staged in LDS (the key area is free once every thread
-  // has its masks, i.e. after the scans' barriers); the row leaves in
+  // The winners (element indices, ascending) were staged in LDS in the
+  // histogram area, free since the last bin selection; they leave in
   // consecutive, coalesced stores instead of each thread's scattered ones.
   __syncthreads();
-  for (int i = tid; i < k; i += kTkThreads) out[i] = (int32_t)sh.keys[i];
+  for (int i = tid; i < k; i += kTkThreads) {
+    const int e = (int)sh.hist[i];
+    if (kMode == kWholeRow) {
+      out[i] = e;
+    } else if (kMode == kChunk) {
+      p.cand_key[cand0 + i] = cached ? sh.keys[kslot(e)] : src_key<false>(src, e);
+      p.cand_pos[cand0 + i] = base + e;
+    } else {
+      out[i] = p.cand_pos[cand0 + e];
+    }
+  }
 }
 
 }  // namespace
 
+int topk_chunk(int num_rows, int max_len, int k) {
+  // Two phases pay off when whole-row work-groups cannot fill the chip and
+  // the rows are longer than the LDS key cache (a whole-row work-group would
+  // re-read them from L2 in every pass; for cached rows one phase is faster,
+  // measured). The candidates of a row (chunks x k) must fit the merge's LDS
+  // key cache, and a chunk its own.
+  if (num_rows > 256 || k > kTkCache / 2 || max_len <= kTkCache) return 0;
+  int chunk = 8192;
+  if (chunk < 2 * k) chunk = 2 * k;
+  const int64_t need = ((int64_t)max_len * k + kTkCache - 1) / kTkCache;   // chunks * k <= kTkCache
+  while (chunk < need) chunk *= 2;
+  if (chunk > kTkCache || max_len < 2 * chunk - chunk / 2) return 0;
+  return chunk;
+}
+
+size_t topk_workspace_bytes(int num_rows, int max_len, int k) {
+  const int chunk = topk_chunk(num_rows, max_len, k);
+  if (chunk == 0) return 0;
+  const int chunks = (max_len + chunk - 1) / chunk;
+  return (size_t)num_rows * chunks * k * (sizeof(uint32_t) + sizeof(int32_t));
+}
+
 hipError_t launch_topk(const TopkParams& p, hipStream_t s) {
   if (p.batch.num_rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3(p.batch.num_rows), dim3(kTkThreads), 0, s, p);
+  if (p.chunk == 0) {
+    hipLaunchKernelGGL(topk_kernel<kWholeRow>, dim3(p.batch.num_rows), dim3(kTkThreads), 0, s, p);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(topk_kernel<kChunk>, dim3(p.batch.num_rows, p.chunks), dim3(kTkThreads), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(topk_kernel<kMerge>, dim3(p.batch.num_rows), dim3(kTkThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -6,7 +6,7 @@ the constructor; `run()` itself allocates nothing.
 """
 import torch
 
-from . import (DSA_BF16, DSA_F32, DSA_OP_MLA_DECODE, DSA_OP_MLA_PREFILL, dsa_indexer_logits,
+from . import (DSA_BF16, DSA_F32, DSA_OP_MLA_DECODE, DSA_OP_MLA_PREFILL, DSA_OP_TOPK, dsa_indexer_logits,
                dsa_topk, dsa_workspace_bytes, make_batch, sparse_mla_decode, sparse_mla_prefill)
 
 
@@ -33,12 +33,14 @@ class DsaStep:
         op = DSA_OP_MLA_PREFILL if self.prefill else DSA_OP_MLA_DECODE
         nbytes = dsa_workspace_bytes(op, self.batch, self.topk, Hm, self.d_latent, mla_dtype)
         self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev) if nbytes else None
+        tk_bytes = dsa_workspace_bytes(DSA_OP_TOPK, self.batch, self.topk, Hm, self.d_latent, mla_dtype)
+        self.topk_workspace = torch.empty(tk_bytes, dtype=torch.uint8, device=dev) if tk_bytes else None
 
     def indexer(self, stream=None):
         dsa_indexer_logits(self.batch, self.q_idx, self.w, self.index_cache, self.logits, stream=stream)
 
     def select(self, stream=None):
-        dsa_topk(self.batch, self.logits, self.topk, self.topk_idx, stream=stream)
+        dsa_topk(self.batch, self.logits, self.topk, self.topk_idx, self.topk_workspace, stream=stream)
 
     def attend(self, stream=None, topk_idx=None):
         fn = sparse_mla_prefill if self.prefill else sparse_mla_decode

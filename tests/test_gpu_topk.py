@@ -1,0 +1,84 @@
+"""GPU top-k against the oracle on crafted logits, bit for bit.
+
+dsa_topk is called directly (no indexer) on rows whose lengths cover the
+short-row rule (visible <= k), rows cached in LDS, rows cut into chunks for
+the two-phase selection of few-row batches, and rows longer than the LDS key
+cache. Values come from a small set with +0 and -0 mixed in, so the k-th value
+is shared by many positions and the lower-position rule decides the set.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from tests import parity  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _run(lengths, k, values, seed):
+    _need_gpu()
+    import sparse_mla_attention_dsa_amd as dsa
+    rng = np.random.default_rng(seed)
+    B = len(lengths)
+    maxlen = max(lengths)
+    stride = (maxlen + 3) // 4 * 4
+    page = 64
+    logits = np.full((B, stride), np.nan, dtype=np.float32)   # columns past a row's length are never read
+    for t, n in enumerate(lengths):
+        logits[t, :n] = values(rng, n)
+    dev = "cuda"
+    lg = torch.from_numpy(logits).to(dev)
+    bt = torch.zeros((B, (maxlen + page - 1) // page), dtype=torch.int32, device=dev)
+    sl = torch.tensor(lengths, dtype=torch.int32, device=dev)
+    batch = dsa.make_batch(bt, sl, page_size=page, num_pages=1, max_seq_len_k=maxlen, max_seq_len_q=1)
+    nbytes = dsa.dsa_workspace_bytes(dsa.DSA_OP_TOPK, batch, k, 0, 0, 0)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+    idx = torch.full((B, k), -7, dtype=torch.int32, device=dev)
+    print(f"\n[topk] B={B} k={k} max_len={maxlen} workspace={nbytes}", flush=True)
+    dsa.dsa_topk(batch, lg, k, idx, ws)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    parity.check_topk_exact(got, logits.astype(np.float64), list(lengths), k, range(B))
+    return nbytes
+
+
+def _ties(rng, n):
+    v = rng.integers(-3, 4, size=n).astype(np.float32) * np.float32(0.5)
+    zeros = rng.random(n) < 0.2
+    v[zeros] = np.where(rng.random(int(zeros.sum())) < 0.5, np.float32(0.0), np.float32(-0.0))
+    return v
+
+
+def _normal(rng, n):
+    return rng.standard_normal(n).astype(np.float32)
+
+
+MIXED = [100, 2048, 2049, 8191, 8192, 12288, 20000, 32768, 40000, 131072]
+
+
+@pytest.mark.parametrize("values", [_ties, _normal], ids=["ties", "normal"])
+def test_two_phase_rows_match_oracle(values):
+    nbytes = _run(MIXED, 2048, values, seed=11)
+    assert nbytes > 0                       # a few long rows: chunks, then their candidates
+
+
+def test_two_phase_k4096():
+    assert _run([5000, 30000, 70000, 4096, 4097], 4096, _ties, seed=12) > 0
+
+
+@pytest.mark.parametrize("k", [1, 7])
+def test_small_odd_k(k):
+    _run([1, 5, 9000, 20000, 50000], k, _ties, seed=13 + k)
+
+
+def test_many_rows_single_phase():
+    rng = np.random.default_rng(17)
+    lengths = [int(x) for x in rng.integers(1, 6000, size=300)]
+    assert _run(lengths, 512, _ties, seed=18) == 0   # enough rows: one work-group per row
