@@ -61,8 +61,10 @@ class Config:
         return len(self.q_lens) > 0
 
 
-# The five workloads the step is specified on, plus the literal "ctx 32k"
-# variant of the ragged decode batch.
+# The five workloads the step is specified on, the literal "ctx 32k" variant
+# of the ragged decode batch, and multi-token decode (speculative verification:
+# next_n query rows per request, row i of a request seeing len - next_n + i + 1
+# keys) over the ragged batch's lengths, pages and keys (same seed).
 CONFIGS = {
     "tiny": Config("tiny", seed=0, batch=1, ctx=(256,), page_size=16, idx_heads=4,
                    idx_dim=32, idx_kind="f32", topk=64, mla_heads=8, d_latent=64,
@@ -78,6 +80,12 @@ CONFIGS = {
                                 note="chunked prefill: 4096 rows on a 16384 prefix"),
     "decode_b64_32k": Config("decode_b64_32k", seed=5, batch=64, ctx=(32768,) * 64,
                              note="batch-64 decode, every ctx 32768"),
+    "mtp_b64x2_ragged": Config("mtp_b64x2_ragged", seed=2, batch=64, ctx_range=(4096, 32768),
+                               q_lens=(2,) * 64,
+                               note="multi-token decode, next_n 2, ragged batch 64, ctx U[4096, 32768]"),
+    "mtp_b64x4_ragged": Config("mtp_b64x4_ragged", seed=2, batch=64, ctx_range=(4096, 32768),
+                               q_lens=(4,) * 64,
+                               note="multi-token decode, next_n 4, ragged batch 64, ctx U[4096, 32768]"),
 }
 
 

@@ -68,6 +68,11 @@ SMALL = [
                  idx_kind="f32", mla_kind="f32"),
     small_config("dec_k1", seed=109, lens=[500, 33], topk=1),
     small_config("dec_empty_row", seed=110, lens=[0, 700], page_size=64, topk=256),
+    # multi-token decode (next_n rows per request, causal inside the request)
+    small_config("mtp_x2", seed=111, lens=[2049, 3000, 130, 5000], q_lens=[2, 2, 2, 2]),
+    small_config("mtp_x4_p16", seed=112, lens=[700, 4100, 2047], q_lens=[4, 4, 4], page_size=16,
+                 topk=512),
+    small_config("mtp_x3_short", seed=113, lens=[3, 2050, 64], q_lens=[3, 3, 3], topk=2048),
 ]
 
 
@@ -90,6 +95,15 @@ def test_full_ragged_batch64_sampled():
 
 def test_full_long_context_128k_sampled():
     _full_check(CONFIGS["decode_b8_128k"], rows=[0, 5])
+
+
+def test_full_multi_token_decode_sampled():
+    cfg = CONFIGS["mtp_b64x2_ragged"]
+    wl = generate(cfg, with_mla=False)
+    lens = wl.seq_lens_k
+    b_min, b_max = int(np.argmin(lens)), int(np.argmax(lens))
+    rows = sorted({2 * b_min, 2 * b_min + 1, 2 * b_max, 2 * b_max + 1, 35})
+    _full_check(cfg, rows=rows)
 
 
 def test_full_prefill_sampled():
