@@ -20,6 +20,8 @@
 // registers before computing anything (16 KB in flight per wave), and writes
 // one fp32 logit per key. The kernel is bound by HBM: 132 bytes of cache per
 // key against 16384 fp8 MACs.
+#include <atomic>
+
 #include "device_common.h"
 #include "dsa_internal.h"
 
@@ -142,30 +144,60 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_fp8_kernel(IndexerPara
   }
 }
 
-// Decode rows (one query row per request): a streaming variant. The keys of
-// all rows are cut into groups of 16 (row t has ceil(visible_t / 16) groups);
-// every wave of a fixed grid takes an equal contiguous share of the flattened
-// group list, whatever the row lengths, and walks it in batches of up to four
-// groups inside one page. The batch list of a wave is built once (lane j holds
-// batch j's row, first group, count, page and row length; all page lookups in
-// one vector load), then the wave streams: the loads of batch j + 1 are issued
-// before the MFMAs of batch j. q and the head weights are reloaded when the
-// row changes (once or twice per wave). Every wave is independent: no barrier
-// after the row prefix sums.
+// Decode rows: a streaming variant. A unit is what shares one key stream: a
+// request's single row (plain decode), or up to two consecutive rows of one
+// request (multi-token decode, where a request carries next_n <= 4 rows and
+// row i sees one key more than row i - 1; the SGLang indexer page scores the
+// next_n rows of a request against the same paged keys). The keys of every
+// unit are cut into groups of 16 (ceil(visible / 16) for its last row); every
+// wave of a fixed grid takes an equal contiguous share of the flattened group
+// list, whatever the lengths, and walks it in batches of up to four groups
+// inside one page. The batch list of a wave is built once (lane j holds batch
+// j's unit, first group, count, page and row lengths; all page lookups in one
+// vector load), then the wave streams: the loads of batch j + 1 are issued
+// before the MFMAs of batch j, and each key group meets the q of every row of
+// its unit. q and the head weights are reloaded when the unit changes (once or
+// twice per wave). Every wave is independent: no barrier after the unit
+// prefix sums.
 constexpr int kStreamThreads = 256;
 constexpr int kStreamWaves = kStreamThreads / kWave;
-constexpr int kStreamMaxRows = 1024;
+constexpr int kStreamMaxUnits = 1024;
 constexpr int kStreamBatch = 4;                                  // groups per batch
+constexpr int kStreamMaxQLen = 4;                                // rows per request, multi-row units
 
-struct StreamBatch {
-  int t, gi, cnt;
-};
+// Unit u of a stream launch with kR rows per unit. kR = 1: unit u is decode
+// row u. kR = 2: unit u is rows 2 (u & 1) and 2 (u & 1) + 1 of request u >> 1
+// (those that exist). Returns the rows' request, first row, count and the
+// visible keys of its first and last row.
+template <int kR>
+__device__ __forceinline__ void stream_unit(const BatchView& bv, int u, int cap, int* b, int* r0, int* nr,
+                                            int* vis_first, int* vis_last) {
+  if (kR == 1) {
+    *b = u;
+    *r0 = u;
+    *nr = 1;
+    *vis_first = *vis_last = visible_keys(bv.seq_lens_k[u], 1, 0, cap);
+    return;
+  }
+  const int req = u >> 1, half = u & 1;
+  const int c0 = bv.cu_seqlens_q[req];
+  const int q_len = bv.cu_seqlens_q[req + 1] - c0;
+  int n = q_len - 2 * half;
+  n = n < 0 ? 0 : (n > 2 ? 2 : n);
+  *b = req;
+  *r0 = c0 + 2 * half;
+  *nr = n;
+  const int len = bv.seq_lens_k[req];
+  *vis_first = n > 0 ? visible_keys(len, q_len, 2 * half, cap) : 0;
+  *vis_last = n > 0 ? visible_keys(len, q_len, 2 * half + n - 1, cap) : 0;
+}
 
+template <int kR, int kAhead>
 __global__ __launch_bounds__(kStreamThreads) void indexer_fp8_stream_kernel(IndexerParams p) {
-  __shared__ int pre[kStreamMaxRows + 1];                        // group prefix over rows
+  __shared__ int pre[kStreamMaxUnits + 1];                       // group prefix over units
   __shared__ int wsum[kStreamWaves];
   const BatchView& bv = p.batch;
-  const int T = bv.num_rows;
+  const int U = kR == 1 ? bv.num_rows : 2 * bv.num_seqs;         // units
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(wave_id());
@@ -176,12 +208,16 @@ __global__ __launch_bounds__(kStreamThreads) void indexer_fp8_stream_kernel(Inde
   if (cap > bv.max_seq_len_k) cap = bv.max_seq_len_k;
   if ((int64_t)cap > p.stride) cap = (int)p.stride;
 
-  // ---- groups per row and their prefix sums ----
+  // ---- groups per unit and their prefix sums ----
   int carry = 0;
-  for (int base = 0; base < T; base += kStreamThreads) {
-    const int t = base + tid;
-    const int vis = t < T ? visible_keys(bv.seq_lens_k[t], 1, 0, cap) : 0;
-    const int cnt = (vis + 15) >> 4;
+  for (int base = 0; base < U; base += kStreamThreads) {
+    const int u = base + tid;
+    int cnt = 0;
+    if (u < U) {
+      int b_, r0_, nr_, vf_, vl_;
+      stream_unit<kR>(bv, u, cap, &b_, &r0_, &nr_, &vf_, &vl_);
+      cnt = (vl_ + 15) >> 4;
+    }
     const int incl = (int)wave_inclusive_scan((uint32_t)cnt);
     if (lane == kWave - 1) wsum[wave] = incl;
     __syncthreads();
@@ -192,23 +228,23 @@ __global__ __launch_bounds__(kStreamThreads) void indexer_fp8_stream_kernel(Inde
       before += (w < wave) ? v : 0;
       tot += v;
     }
-    if (t < T) pre[t + 1] = carry + before + incl;
+    if (u < U) pre[u + 1] = carry + before + incl;
     carry += tot;
     __syncthreads();
   }
   if (tid == 0) pre[0] = 0;
   __syncthreads();
 
-  const int N = pre[T];
+  const int N = pre[U];
   const int W = gridDim.x * kStreamWaves;
   const int wg = blockIdx.x * kStreamWaves + wave;
   int a = (int)((int64_t)N * wg / W);
   const int a_end = (int)((int64_t)N * (wg + 1) / W);
   if (a >= a_end) return;
-  // row of group a: the largest t with pre[t] <= a (rows without groups are passed over)
+  // unit of group a: the largest t with pre[t] <= a (units without groups are passed over)
   int t = 0;
   {
-    int lo = 0, hi = T - 1;
+    int lo = 0, hi = U - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (pre[mid] <= a) lo = mid; else hi = mid - 1;
@@ -226,7 +262,7 @@ __global__ __launch_bounds__(kStreamThreads) void indexer_fp8_stream_kernel(Inde
     int bt_t = 0, bt_gi = 0, bt_cnt = 0, nb = 0;
     while (a < a_end && nb < kWave) {
       int n_t = pre[t + 1] - pre[t];
-      while (gi >= n_t) {                                        // next row with groups
+      while (gi >= n_t) {                                        // next unit with groups
         ++t;
         gi = 0;
         n_t = pre[t + 1] - pre[t];
@@ -240,92 +276,117 @@ __global__ __launch_bounds__(kStreamThreads) void indexer_fp8_stream_kernel(Inde
       gi = gend;
       ++nb;
     }
-    // pages and row lengths of every batch in one go
-    int bt_page = -1, bt_vis = 0;
+    // pages, first rows and row lengths of every batch in one go
+    int bt_page = -1, bt_r0 = 0, bt_nr = 0, bt_vf = 0, bt_vl = 0;
     if (lane < nb) {
-      const int pi = bt_gi / gpp;
-      bt_page = bv.block_table[(int64_t)bt_t * bv.max_pages_per_seq + pi];
-      bt_vis = visible_keys(bv.seq_lens_k[bt_t], 1, 0, cap);
+      int b_;
+      stream_unit<kR>(bv, bt_t, cap, &b_, &bt_r0, &bt_nr, &bt_vf, &bt_vl);
+      bt_page = bv.block_table[(int64_t)b_ * bv.max_pages_per_seq + bt_gi / gpp];
     }
 
-    auto batch_of = [&](int j, int* bt, int* bg, int* bc, int* bp, int* bvv) {
-      *bt = __builtin_amdgcn_readlane(bt_t, j);
-      *bg = __builtin_amdgcn_readlane(bt_gi, j);
-      *bc = __builtin_amdgcn_readlane(bt_cnt, j);
-      *bp = __builtin_amdgcn_readlane(bt_page, j);
-      *bvv = __builtin_amdgcn_readlane(bt_vis, j);
+    struct Batch { int t, gi, cnt, page, r0, nr, vf, vl; };
+    auto batch_of = [&](int j) {
+      Batch x;
+      x.t = __builtin_amdgcn_readlane(bt_t, j);
+      x.gi = __builtin_amdgcn_readlane(bt_gi, j);
+      x.cnt = __builtin_amdgcn_readlane(bt_cnt, j);
+      x.page = __builtin_amdgcn_readlane(bt_page, j);
+      x.r0 = __builtin_amdgcn_readlane(bt_r0, j);
+      x.nr = kR == 1 ? 1 : __builtin_amdgcn_readlane(bt_nr, j);
+      x.vf = __builtin_amdgcn_readlane(bt_vf, j);
+      x.vl = kR == 1 ? x.vf : __builtin_amdgcn_readlane(bt_vl, j);
+      return x;
     };
     // key operands (lane (c, g): key 16u + c of the batch, bytes [32g, 32g + 32)) and scales
-    auto load_batch = [&](int bg, int bc, int bp, i32x8 (&kb)[kStreamBatch], float (&sg)[kStreamBatch]) {
-      const bool okp = bp >= 0 && bp < bv.num_pages;
-      const uint8_t* pg = cache + (int64_t)(okp ? bp : 0) * p.page_bytes;
+    auto load_batch = [&](const Batch& x, i32x8 (&kb)[kStreamBatch], float (&sg)[kStreamBatch]) {
+      const bool okp = x.page >= 0 && x.page < bv.num_pages;
+      const uint8_t* pg = cache + (int64_t)(okp ? x.page : 0) * p.page_bytes;
 #pragma unroll
       for (int u = 0; u < kStreamBatch; ++u) {
-        const int uu = u < bc ? u : 0;                           // past the batch: re-read group 0
-        const int slot = (16 * (bg + uu)) % P + c;
+        const int uu = u < x.cnt ? u : 0;                        // past the batch: re-read group 0
+        const int slot = (16 * (x.gi + uu)) % P + c;
         kb[u] = *reinterpret_cast<const i32x8*>(pg + (int64_t)slot * kIdxDim + 32 * g);
         sg[u] = *reinterpret_cast<const float*>(pg + scale_off + 4 * slot);
       }
     };
 
-    i32x8 qa[4];
-    float wv[16];
-    int q_row = -1;
-    auto load_row = [&](int rt) {
-      const uint8_t* qr = static_cast<const uint8_t*>(p.q) + (int64_t)rt * (kIdxHeads * kIdxDim);
+    // q of the unit's rows as 16-head A operands (lane (c, g): head 16m + c,
+    // bytes [32g, 32g + 32)) and their head weights in accumulator order
+    i32x8 qa[kR][4];
+    float wv[kR][16];
+    int q_unit = -1;
+    auto load_unit = [&](const Batch& x) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
-        qa[m] = *reinterpret_cast<const i32x8*>(qr + (16 * m + c) * kIdxDim + 32 * g);
-      const float* wrow = p.w + (int64_t)rt * kIdxHeads;
+      for (int r = 0; r < kR; ++r) {
+        if (r < x.nr) {
+          const int row = x.r0 + r;
+          const uint8_t* qr = static_cast<const uint8_t*>(p.q) + (int64_t)row * (kIdxHeads * kIdxDim);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const f32x4 w4 = *reinterpret_cast<const f32x4*>(wrow + 16 * m + 4 * g);
+          for (int m = 0; m < 4; ++m)
+            qa[r][m] = *reinterpret_cast<const i32x8*>(qr + (16 * m + c) * kIdxDim + 32 * g);
+          const float* wrow = p.w + (int64_t)row * kIdxHeads;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wv[4 * m + i] = w4[i];
+          for (int m = 0; m < 4; ++m) {
+            const f32x4 w4 = *reinterpret_cast<const f32x4*>(wrow + 16 * m + 4 * g);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wv[r][4 * m + i] = w4[i];
+          }
+        }
       }
-      q_row = rt;
+      q_unit = x.t;
     };
 
-    // one batch in flight ahead of the one being computed
-    int ct, cg, cc, cp, cv;
-    batch_of(0, &ct, &cg, &cc, &cp, &cv);
-    i32x8 k0[kStreamBatch];
-    float s0[kStreamBatch];
-    load_batch(cg, cc, cp, k0, s0);
-    load_row(ct);
+    // kAhead batches in flight ahead of the one being computed
+    Batch bq[kAhead + 1];
+    i32x8 kb[kAhead + 1][kStreamBatch];
+    float sg[kAhead + 1][kStreamBatch];
+#pragma unroll
+    for (int d = 0; d < kAhead; ++d) {
+      if (d < nb) {
+        bq[d] = batch_of(d);
+        load_batch(bq[d], kb[d], sg[d]);
+      }
+    }
+    load_unit(bq[0]);
     for (int j = 0; j < nb; ++j) {
-      int nt_ = 0, ng = 0, nc = 0, np = -1, nv = 0;
-      i32x8 k1[kStreamBatch];
-      float s1[kStreamBatch];
-      const bool more = j + 1 < nb;
-      if (more) {
-        batch_of(j + 1, &nt_, &ng, &nc, &np, &nv);
-        load_batch(ng, nc, np, k1, s1);
+      if (j + kAhead < nb) {
+        bq[kAhead] = batch_of(j + kAhead);
+        load_batch(bq[kAhead], kb[kAhead], sg[kAhead]);
       }
-      if (ct != q_row) load_row(ct);
-      // ---- logits of batch j ----
-      const bool okp = cp >= 0 && cp < bv.num_pages;
-      float* out = p.logits + (int64_t)ct * p.stride;
+      const Batch& cur = bq[0];
+      if (cur.t != q_unit) load_unit(cur);
+      // ---- logits of batch j, for every row of its unit ----
+      const bool okp = cur.page >= 0 && cur.page < bv.num_pages;
 #pragma unroll
-      for (int u = 0; u < kStreamBatch; ++u) {
-        if (u >= cc) break;
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        float part = 0.f;
+      for (int r = 0; r < kR; ++r) {
+        if (r >= cur.nr) break;
+        // rows of a unit see one key more each; the last one sees vl
+        const int vis = (r == cur.nr - 1) ? cur.vl : cur.vf;
+        float* out = p.logits + (int64_t)(cur.r0 + r) * p.stride;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const f32x4 acc = mfma_fp8_16x16x128(qa[m], k0[u], zero);
+        for (int u = 0; u < kStreamBatch; ++u) {
+          if (u >= cur.cnt) break;
+          const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+          float part = 0.f;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) part = fmaf(wv[4 * m + i], relu_bits(acc[i]), part);
+          for (int m = 0; m < 4; ++m) {
+            const f32x4 acc = mfma_fp8_16x16x128(qa[r][m], kb[0][u], zero);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) part = fmaf(wv[r][4 * m + i], relu_bits(acc[i]), part);
+          }
+          part += shfl_xor_f(part, 16);
+          part += shfl_xor_f(part, 32);
+          const int s = 16 * (cur.gi + u) + c;
+          if (g == 0 && s < vis) out[s] = okp ? part * sg[0][u] : -INFINITY;
         }
-        part += shfl_xor_f(part, 16);
-        part += shfl_xor_f(part, 32);
-        const int s = 16 * (cg + u) + c;
-        if (g == 0 && s < cv) out[s] = okp ? part * s0[u] : -INFINITY;
       }
-      if (!more) break;
-      ct = nt_; cg = ng; cc = nc; cp = np; cv = nv;
+      if (j + 1 >= nb) break;
 #pragma unroll
-      for (int u = 0; u < kStreamBatch; ++u) { k0[u] = k1[u]; s0[u] = s1[u]; }
+      for (int d = 0; d < kAhead; ++d) {
+        bq[d] = bq[d + 1];
+#pragma unroll
+        for (int u = 0; u < kStreamBatch; ++u) { kb[d][u] = kb[d + 1][u]; sg[d][u] = sg[d + 1][u]; }
+      }
     }
   }
 }
@@ -642,18 +703,55 @@ __global__ __launch_bounds__(kF32Block) void indexer_f32_kernel(IndexerParams p)
   out[s] = acc * sigma;
 }
 
+// Work-groups of a stream kernel that the current device holds at once: CUs
+// times the occupancy the kernel's registers and LDS allow. Queried once per
+// device and kernel (host calls only, nothing is enqueued).
+template <int kR, int kAhead>
+int resident_wgs() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
+  if (dev >= 0) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int cus = 0, per_cu = 0;
+  if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, indexer_fp8_stream_kernel<kR, kAhead>,
+                                                   kStreamThreads, 0) != hipSuccess ||
+      cus < 1 || per_cu < 1) {
+    (void)hipGetLastError();
+    return 256 * (kR == 1 ? 3 : 2);                              // MI355X: 256 CUs
+  }
+  const int v = cus * per_cu;
+  if (dev >= 0) cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
 }  // namespace
 
 hipError_t launch_indexer_fp8(const IndexerParams& p, hipStream_t s) {
   const int chunks = (p.batch.max_seq_len_k + kIdxChunk - 1) / kIdxChunk;
   if (p.batch.num_rows == 0 || chunks == 0) return hipSuccess;
-  if (p.batch.cu_seqlens_q == nullptr && p.batch.num_rows <= kStreamMaxRows) {
-    // about 32 groups per wave, at most three work-groups per CU (one round)
-    const int64_t groups = (int64_t)p.batch.num_rows * ((p.batch.max_seq_len_k + 15) / 16);
+  const bool decode = p.batch.cu_seqlens_q == nullptr && p.batch.num_rows <= kStreamMaxUnits;
+  const bool multi = p.batch.cu_seqlens_q != nullptr && p.batch.max_seq_len_q <= kStreamMaxQLen &&
+                     2 * p.batch.num_seqs <= kStreamMaxUnits;
+  if (decode || multi) {
+    // about 32 groups per wave, and no more work-groups than are resident at
+    // once (one round: a second round would start late and finish last)
+    const int64_t units = decode ? p.batch.num_rows : std::min<int64_t>(p.batch.num_rows, 2LL * p.batch.num_seqs);
+    const int64_t groups = units * ((p.batch.max_seq_len_k + 15) / 16);
     int64_t wgs = (groups / 32 + kStreamWaves - 1) / kStreamWaves;
-    if (wgs > 768) wgs = 768;
+    const int resident = decode ? resident_wgs<1, 1>() : resident_wgs<2, 1>();
+    if (wgs > resident) wgs = resident;
     if (wgs < 1) wgs = 1;
-    hipLaunchKernelGGL(indexer_fp8_stream_kernel, dim3((unsigned)wgs), dim3(kStreamThreads), 0, s, p);
+    if (decode)
+      hipLaunchKernelGGL(HIP_KERNEL_NAME(indexer_fp8_stream_kernel<1, 1>), dim3((unsigned)wgs),
+                         dim3(kStreamThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL(HIP_KERNEL_NAME(indexer_fp8_stream_kernel<2, 1>), dim3((unsigned)wgs),
+                         dim3(kStreamThreads), 0, s, p);
     return hipGetLastError();
   }
   if (p.batch.cu_seqlens_q != nullptr && p.batch.num_seqs <= kPfMaxSeqs && p.stride <= kPfMaxStride) {
