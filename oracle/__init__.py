@@ -41,6 +41,11 @@ Parity status per function (what pins it; see tests/test_oracle_*.py):
   attention when k >= context, split + LSE merge, absorption identity).
 * dsa.lse_merge .......................... pinned (associativity against a
   single pass, closed form for equal halves).
+* quant.encode_e4m3fn / quant_rows /
+  quant_index_q / store_index_k .......... pinned (every finite code round
+  trips, ties and near-ties between all neighbours, torch's CPU conversion on
+  a million values, amax lands on 448, power-of-two scale invariance, half-step
+  error bound, paged store read back through dsa.gather_index_keys).
 """
 
 from .formats import decode_bf16, decode_e4m3fn, e4m3fn_table  # noqa: F401
@@ -58,3 +63,4 @@ from .dsa import (  # noqa: F401
     topk,
     topk_row,
 )
+from .quant import encode_e4m3fn, quant_index_q, quant_rows, store_index_k  # noqa: F401
