@@ -8,6 +8,11 @@
  *   sparse_mla_decode   sparse MLA attention over the selected latent rows
  *   sparse_mla_prefill  (decode: one query row per request; prefill: many)
  *
+ * and two for the indexer's inputs, the step before the scores:
+ *
+ *   dsa_quant_index_q   fp8 index queries, per-head scale folded into the gates
+ *   dsa_store_index_k   fp8 quantization of new index keys + their paged store
+ *
  * Sources: the SGLang "dsa_indexer.py" page (Indexer._get_topk_paged calls the
  * paged fp8 MQA-logits kernel with q_fp8 [T,H,128], the 132-byte-per-token
  * index cache, weights [T,H], seqlens and block tables, then topk_transform),
@@ -120,6 +125,47 @@ dsa_status_t dsa_indexer_logits(const dsa_batch_t *batch,
                                 int32_t num_heads, int32_t head_dim,
                                 float *logits, int64_t logits_row_stride,
                                 dsa_stream_t stream);
+
+/*
+ * dsa_quant_index_q - fp8 index queries and their head gates, the input side
+ * of dsa_indexer_logits (SGLang page, Indexer.forward_cuda: act_quant of the
+ * bf16 query into (q_fp8, q_scale); _get_logits_head_gate: gates times q_scale).
+ * For each row t and head h, over the head's D = 128 elements:
+ *
+ *   s[t,h]     = max(max_d |q[t,h,d]|, 1e-30) / 448                 (fp32)
+ *   q8[t,h,d]  = E4M3FN(q[t,h,d] / s[t,h])   fp32 quotient, nearest, ties to even
+ *   w_eff[t,h] = w[t,h] * s[t,h]                                    (fp32)
+ *
+ * (act_quant is not on the pages; this is the reading with one fp32 scale per
+ * 128-wide block.) A magnitude that rounds past 448 becomes NaN (E4M3FN has no
+ * infinity); with these scales finite inputs never do. A block holding NaN
+ * gets a NaN scale and NaN codes (their sign bit unspecified).
+ *
+ * q:     [T, H, 128] bf16, 16-byte aligned.   w: [T, H] fp32 (the n_heads^-0.5
+ *        and softmax factors already applied).
+ * q8:    [T, H, 128] E4M3FN codes, 8-byte aligned.   w_eff: [T, H] fp32; may be w.
+ * num_rows = T >= 0, 1 <= num_heads, head_dim must be 128.
+ */
+dsa_status_t dsa_quant_index_q(const void *q, const float *w, int32_t num_rows, int32_t num_heads,
+                               int32_t head_dim, void *q8, float *w_eff, dsa_stream_t stream);
+
+/*
+ * dsa_store_index_k - fp8 quantization of a step's new index keys and their
+ * paged store (SGLang page, Indexer._store_index_k_cache: act_quant(key) and
+ * set_index_k_scale_buffer at out_cache_loc). Key i gets the block scale and
+ * codes of dsa_quant_index_q (sigma_i and k8[i, :]) and is written at slot
+ * s = slot_mapping[i], i.e. page s / P, position s % P of index_cache: its 128
+ * codes at byte 128 * (s % P) of the page, sigma_i at byte 128 * P + 4 * (s % P)
+ * (the fp8 layout dsa_indexer_logits reads). Negative slots and slots
+ * >= num_pages * P are skipped (padding tokens). Slots must be distinct.
+ *
+ * key: [N, 128] bf16, 16-byte aligned.   slot_mapping: [N] int64.
+ * index_cache: [num_pages, 132 * P] bytes, 16-byte aligned; P a positive
+ *              multiple of 16.   num_tokens = N >= 0, head_dim must be 128.
+ */
+dsa_status_t dsa_store_index_k(const void *key, int32_t num_tokens, int32_t head_dim,
+                               const int64_t *slot_mapping, int32_t page_size, int32_t num_pages,
+                               void *index_cache, dsa_stream_t stream);
 
 /*
  * dsa_topk - per-row top-k selection (SGLang page: topk_transform after the

@@ -18,7 +18,7 @@ __all__ = [
     "DSA_OK", "DSA_F32", "DSA_BF16", "DSA_FP8_E4M3", "DSA_OP_TOPK", "DSA_OP_MLA_DECODE",
     "DSA_OP_MLA_PREFILL", "DsaError", "DsaBatch", "lib", "library_path", "make_batch",
     "dsa_indexer_logits", "dsa_topk", "sparse_mla_decode", "sparse_mla_prefill",
-    "dsa_workspace_bytes", "dsa_version", "EXPORTED_SYMBOLS",
+    "dsa_quant_index_q", "dsa_store_index_k", "dsa_workspace_bytes", "dsa_version", "EXPORTED_SYMBOLS",
 ]
 
 DSA_OK, DSA_ERR_INVALID_ARGUMENT, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE_TOO_SMALL, DSA_ERR_HIP = range(5)
@@ -27,6 +27,7 @@ DSA_OP_TOPK, DSA_OP_MLA_DECODE, DSA_OP_MLA_PREFILL = range(3)
 
 EXPORTED_SYMBOLS = (
     "dsa_indexer_logits", "dsa_topk", "sparse_mla_decode", "sparse_mla_prefill",
+    "dsa_quant_index_q", "dsa_store_index_k",
     "dsa_workspace_bytes", "dsa_status_string", "dsa_last_error", "dsa_version",
 )
 
@@ -81,6 +82,10 @@ def lib():
         f = getattr(L, name)
         f.argtypes = [P, V, V, I32, V, I32, I32, I32, I32, F32, V, V, V, SZ, V]
         f.restype = I32
+    L.dsa_quant_index_q.argtypes = [V, V, I32, I32, I32, V, V, V]
+    L.dsa_quant_index_q.restype = I32
+    L.dsa_store_index_k.argtypes = [V, I32, I32, V, I32, I32, V, V]
+    L.dsa_store_index_k.restype = I32
     L.dsa_workspace_bytes.argtypes = [I32, P, I32, I32, I32, I32]
     L.dsa_workspace_bytes.restype = SZ
     L.dsa_status_string.argtypes = [I32]
@@ -183,6 +188,20 @@ def sparse_mla_prefill(batch, q, kv_cache, topk_idx, softmax_scale, out, lse=Non
                        *, d_latent=None, stream=None):
     _mla(lib().sparse_mla_prefill, batch, q, kv_cache, topk_idx, softmax_scale, out, lse, workspace,
          d_latent, stream)
+
+
+def dsa_quant_index_q(q, w, q8, w_eff, stream=None):
+    """q [T, H, 128] bf16 -> q8 [T, H, 128] fp8 codes and w_eff = w * per-head scale."""
+    T, H, D = (int(x) for x in q.shape)
+    _check(lib().dsa_quant_index_q(_ptr(q), _ptr(w), T, H, D, _ptr(q8), _ptr(w_eff), _stream(stream)))
+
+
+def dsa_store_index_k(key, slot_mapping, index_cache, page_size, stream=None):
+    """Quantize key [N, 128] bf16 per token and store it at slot_mapping [N] int64
+    into the paged index cache [num_pages, 132 * page_size] (uint8)."""
+    N, D = (int(x) for x in key.shape)
+    _check(lib().dsa_store_index_k(_ptr(key), N, D, _ptr(slot_mapping), int(page_size),
+                                   int(index_cache.shape[0]), _ptr(index_cache), _stream(stream)))
 
 
 def dsa_workspace_bytes(op, batch, k, num_heads, d_latent, dtype):

@@ -214,6 +214,48 @@ dsa_status_t dsa_indexer_logits(const dsa_batch_t* batch, const void* q, dsa_dty
                   "indexer launch");
 }
 
+dsa_status_t dsa_quant_index_q(const void* q, const float* w, int32_t num_rows, int32_t num_heads,
+                               int32_t head_dim, void* q8, float* w_eff, dsa_stream_t stream) {
+  if (num_rows < 0 || num_heads < 1)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "num_rows %d < 0 or num_heads %d < 1", num_rows, num_heads);
+  if (head_dim != kIdxDim) return fail(DSA_ERR_UNSUPPORTED, "head_dim %d (128 only)", head_dim);
+  if (num_rows == 0) return ok();
+  if (!q || !w || !q8 || !w_eff) return fail(DSA_ERR_INVALID_ARGUMENT, "q / w / q8 / w_eff is NULL");
+  if (reinterpret_cast<uintptr_t>(q) % 16 != 0 || reinterpret_cast<uintptr_t>(q8) % 8 != 0)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "q must be 16-byte and q8 8-byte aligned");
+  QuantQParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.w = w;
+  p.q8 = static_cast<uint8_t*>(q8);
+  p.w_eff = w_eff;
+  p.rows = (int64_t)num_rows * num_heads;
+  return from_hip(launch_quant_index_q(p, reinterpret_cast<hipStream_t>(stream)), "q quantization launch");
+}
+
+dsa_status_t dsa_store_index_k(const void* key, int32_t num_tokens, int32_t head_dim,
+                               const int64_t* slot_mapping, int32_t page_size, int32_t num_pages,
+                               void* index_cache, dsa_stream_t stream) {
+  if (num_tokens < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "num_tokens %d < 0", num_tokens);
+  if (head_dim != kIdxDim) return fail(DSA_ERR_UNSUPPORTED, "head_dim %d (128 only)", head_dim);
+  if (page_size < 16 || page_size % 16 != 0)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "page_size %d is not a positive multiple of 16", page_size);
+  if (num_pages < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "num_pages %d < 0", num_pages);
+  if (num_tokens == 0) return ok();
+  if (!key || !slot_mapping || !index_cache)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "key / slot_mapping / index_cache is NULL");
+  if (reinterpret_cast<uintptr_t>(key) % 16 != 0 || reinterpret_cast<uintptr_t>(index_cache) % 16 != 0)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "key and index_cache must be 16-byte aligned");
+  StoreKParams p;
+  p.key = static_cast<const uint16_t*>(key);
+  p.slot_mapping = slot_mapping;
+  p.cache = static_cast<uint8_t*>(index_cache);
+  p.num_tokens = num_tokens;
+  p.page_bytes = (int64_t)page_size * (kIdxDim + 4);
+  p.page_size = page_size;
+  p.num_pages = num_pages;
+  return from_hip(launch_store_index_k(p, reinterpret_cast<hipStream_t>(stream)), "index-K store launch");
+}
+
 dsa_status_t dsa_topk(const dsa_batch_t* batch, const float* logits, int64_t logits_row_stride,
                       int32_t k, int32_t* topk_idx, void* workspace, size_t workspace_bytes,
                       dsa_stream_t stream) {

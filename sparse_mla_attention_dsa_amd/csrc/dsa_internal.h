@@ -86,6 +86,28 @@ int mla_entries_per_split(int k, int splits);
 int topk_chunk(int num_rows, int max_len, int k);
 size_t topk_workspace_bytes(int num_rows, int max_len, int k);
 
+// fp8 quantization of the index query rows (T * H rows of 128) and gates
+struct QuantQParams {
+  const uint16_t* q;        // [rows, 128] bf16
+  const float* w;           // [rows]
+  uint8_t* q8;              // [rows, 128] E4M3FN codes
+  float* w_eff;             // [rows]
+  int64_t rows;
+};
+
+// fp8 quantization of new index keys and their paged store
+struct StoreKParams {
+  const uint16_t* key;            // [num_tokens, 128] bf16
+  const int64_t* slot_mapping;    // [num_tokens]
+  uint8_t* cache;                 // [num_pages, page_bytes]
+  int64_t num_tokens;
+  int64_t page_bytes;             // page_size * 128 + 4 * page_size
+  int32_t page_size;
+  int32_t num_pages;
+};
+
+hipError_t launch_quant_index_q(const QuantQParams& p, hipStream_t s);
+hipError_t launch_store_index_k(const StoreKParams& p, hipStream_t s);
 hipError_t launch_indexer_fp8(const IndexerParams& p, hipStream_t s);
 hipError_t launch_indexer_f32(const IndexerParams& p, hipStream_t s);
 hipError_t launch_topk(const TopkParams& p, hipStream_t s);

@@ -183,3 +183,23 @@ def test_python_binding_raises_on_errors(L):
         dsa.dsa_topk(batch, logits, 8, idx, stream=0)
     assert e.value.status == dsa.DSA_ERR_INVALID_ARGUMENT
     assert "page_size" in str(e.value)
+
+
+def test_quant_entry_points_validate_on_the_host(L):
+    V = ctypes.c_void_p
+    ok = dsa.DSA_OK
+    assert L.dsa_quant_index_q(None, None, 0, 64, 128, None, None, None) == ok      # nothing to do
+    assert L.dsa_quant_index_q(V(0x100), V(0x200), 4, 64, 64, V(0x300), V(0x400), None) == dsa.DSA_ERR_UNSUPPORTED
+    assert L.dsa_quant_index_q(None, V(0x200), 4, 64, 128, V(0x300), V(0x400), None) == \
+        dsa.DSA_ERR_INVALID_ARGUMENT
+    assert L.dsa_quant_index_q(V(0x108), V(0x200), 4, 64, 128, V(0x300), V(0x400), None) == \
+        dsa.DSA_ERR_INVALID_ARGUMENT                                                 # q misaligned
+    assert L.dsa_quant_index_q(V(0x100), V(0x200), -1, 64, 128, V(0x300), V(0x400), None) == \
+        dsa.DSA_ERR_INVALID_ARGUMENT
+    assert L.dsa_store_index_k(None, 0, 128, None, 64, 4, None, None) == ok
+    assert L.dsa_store_index_k(V(0x100), 3, 128, V(0x200), 48 + 1, 4, V(0x300), None) == \
+        dsa.DSA_ERR_INVALID_ARGUMENT                                                 # page size
+    assert L.dsa_store_index_k(V(0x100), 3, 96, V(0x200), 64, 4, V(0x300), None) == dsa.DSA_ERR_UNSUPPORTED
+    assert L.dsa_store_index_k(V(0x100), 3, 128, None, 64, 4, V(0x300), None) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert L.dsa_store_index_k(V(0x100), 3, 128, V(0x200), 64, 4, V(0x308), None) == \
+        dsa.DSA_ERR_INVALID_ARGUMENT                                                 # cache misaligned
