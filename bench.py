@@ -61,6 +61,48 @@ def algorithmic_work(wl):
     }
 
 
+def time_input_side(wl, K, stream):
+    """Average launch time of the indexer's input side for this batch, outside
+    the step: dsa_quant_index_q on every query row (bf16 [T, H, 128] in) and
+    dsa_store_index_k of one new key per query row, each key on its own page
+    (a scratch cache, so the step's cache keeps its keys)."""
+    import torch
+    import sparse_mla_attention_dsa_amd as dsa
+    cfg = wl.cfg
+    if cfg.idx_kind != "fp8":
+        return None
+    T, H, D, P = wl.num_rows, cfg.idx_heads, cfg.idx_dim, cfg.page_size
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    q = torch.randn((T, H, D), generator=gen, device="cuda").to(torch.bfloat16)
+    w = torch.randn((T, H), generator=gen, device="cuda") / 8.0
+    q8 = torch.empty((T, H, D), dtype=torch.uint8, device="cuda")
+    w_eff = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    key = torch.randn((T, D), generator=gen, device="cuda").to(torch.bfloat16)
+    cache = torch.zeros((T, (D + 4) * P), dtype=torch.uint8, device="cuda")
+    slots = (torch.arange(T, device="cuda", dtype=torch.int64) * P
+             + torch.randint(0, P, (T,), generator=gen, device="cuda"))
+    out = {}
+    for name, fn, nbytes in (
+            ("quant_index_q", lambda: dsa.dsa_quant_index_q(q, w, q8, w_eff), T * H * (2 * D + 4 + D + 4)),
+            ("store_index_k", lambda: dsa.dsa_store_index_k(key, slots, cache, P), T * (2 * D + 8 + D + 4))):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        try:
+            torch.cuda._sleep(20_000_000)                    # the host queues the launches meanwhile
+        except Exception:
+            pass
+        e0.record(stream)
+        for _ in range(K):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / K
+        out[name] = {"us": us, "algorithmic_bytes": nbytes, "hbm_gbps": nbytes / (us * 1e-6) / 1e9}
+    return out
+
+
 def cpu_baseline(wl, budget_s=12.0, max_rows=4096):
     """Oracle (float64 numpy) on whole rows of the workload until ~budget_s of CPU work."""
     import oracle
@@ -194,6 +236,8 @@ def main():
                 for j, (name, _) in enumerate(stages)}
     print(f"[bench] timed {K} steps: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
 
+    input_side = time_input_side(wl, K, stream)
+
     work = algorithmic_work(wl)
     tokens_per_s = wl.num_rows / (ms_per_step * 1e-3)
     kernels = {}
@@ -249,6 +293,7 @@ def main():
                    "mla": f"{cfg.mla_heads} heads x {cfg.d_latent}+{cfg.d_rope} {cfg.mla_kind}"},
         "sparse_attn_hbm_gbps": kernels["sparse_mla"]["hbm_gbps"],
         "stages": kernels,
+        "input_side": input_side,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
