@@ -39,6 +39,9 @@ Parity status per function (what pins it; see tests/test_oracle_*.py):
 * dsa.sparse_mla ......................... pinned (closed forms for one index
   and q = 0, softmax sums to one, equality with an independently coded dense
   attention when k >= context, split + LSE merge, absorption identity).
+* dsa.sparse_mla, fp8 latent cache ........ pinned (exact reduction to the
+  float path with power-of-two scales; moving factors between the softmax,
+  query and cache scales).
 * dsa.lse_merge .......................... pinned (associativity against a
   single pass, closed form for equal halves).
 * quant.encode_e4m3fn / quant_rows /

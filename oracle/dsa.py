@@ -158,14 +158,23 @@ def topk(logits_by_row, visible_by_row, k):
     return {t: topk_row(logits_by_row[t], visible_by_row[t], k) for t in logits_by_row}
 
 
+def _decode_latent(raw, kind):
+    if kind == "bf16":
+        return decode_bf16(raw)
+    if kind == "fp8":
+        return decode_e4m3fn(raw)
+    return np.asarray(raw, dtype=np.float64)
+
+
 def gather_latent_rows(latent_cache, block_table_row, positions, page_size, kind):
-    """Latent rows C[p] (float64 [len(positions), Dl+Dr]) through the block table."""
+    """Latent rows C[p] (float64 [len(positions), Dl+Dr]) through the block
+    table; for kind "fp8" the decoded E4M3 codes (the caller applies the scale)."""
     rows = []
     for p in positions:
         page = int(block_table_row[int(p) // page_size])
         slot = int(p) % page_size
         raw = latent_cache[page, slot]
-        rows.append(decode_bf16(raw) if kind == "bf16" else np.asarray(raw, dtype=np.float64))
+        rows.append(_decode_latent(raw, kind))
     if not rows:
         return np.zeros((0, latent_cache.shape[-1]), dtype=np.float64)
     return np.stack(rows)
@@ -203,12 +212,19 @@ def sparse_mla_row(q_row, rows_c, d_latent, scale, return_probs=False):
 
 
 def sparse_mla(q, latent_cache, topk_idx, block_table, seq_lens_k, cu_seqlens_q,
-               page_size, d_latent, scale, kind, rows=None):
+               page_size, d_latent, scale, kind, rows=None, q_scale=1.0, kv_scale=1.0):
     """Sparse MLA for every query row (or the listed rows).
 
-    q: [T, Hm, Dqk] bf16 bits (uint16) for kind "bf16", float32 for "f32".
+    q: [T, Hm, Dqk] bf16 bits (uint16) for kind "bf16", float32 for "f32",
+    E4M3 codes (uint8) for "fp8".
     topk_idx: [T, k] logical positions, -1 = empty slot.
     Returns {row: (out float64 [Hm, Dl], lse float64 [Hm])}.
+
+    fp8 (vLLM MLA page, the decode path under `fp8_attention`: the absorbed
+    query goes through `scaled_fp8_quant` with the layer's q scale, and the
+    cache is written in fp8 with the layer's k scale): one scale per tensor,
+    so the query is codes * q_scale and every cached row codes * kv_scale;
+    the attention is then the same as for the other kinds, on those values.
     """
     info = row_layout(seq_lens_k, cu_seqlens_q)
     wanted = range(len(info)) if rows is None else rows
@@ -217,7 +233,10 @@ def sparse_mla(q, latent_cache, topk_idx, block_table, seq_lens_k, cu_seqlens_q,
         b = info[t].seq
         pos = _valid_positions(topk_idx[t], int(seq_lens_k[b]))
         rows_c = gather_latent_rows(latent_cache, block_table[b], pos, page_size, kind)
-        q_row = decode_bf16(q[t]) if kind == "bf16" else np.asarray(q[t], dtype=np.float64)
+        q_row = _decode_latent(q[t], kind)
+        if kind == "fp8":
+            rows_c = rows_c * float(kv_scale)
+            q_row = q_row * float(q_scale)
         res[t] = sparse_mla_row(q_row, rows_c, d_latent, scale)
     return res
 

@@ -161,3 +161,43 @@ def test_hand_example_rejects_plausible_mistakes(golden_dir, variant, monkeypatc
                                 np.array([3]), None, 2, 2, 1.0, "f32")[0]
     ok = np.allclose(res[0], ex["expected_out"]) and np.allclose(res[1], ex["expected_lse"])
     assert not ok
+
+
+def _fp8_case(seed, n_pages=6, P=16, Hm=8, Dl=64, Dr=16, k=40):
+    rng = np.random.default_rng(seed)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    latent = rng.choice(finite, size=(n_pages, P, Dl + Dr))
+    q = rng.choice(finite, size=(2, Hm, Dl + Dr))
+    bt = rng.permutation(n_pages).astype(np.int32).reshape(2, n_pages // 2)
+    lens = np.array([P * (n_pages // 2) - 5, P * (n_pages // 2)])
+    idx = np.stack([rng.choice(int(n), size=k, replace=False) for n in lens]).astype(np.int32)
+    idx[0, :3] = -1
+    return latent, q, idx, bt, lens, P, Dl
+
+
+def test_fp8_cache_reduces_to_the_float_path():
+    """With power-of-two scales the dequantized values are exact in float32,
+    so the fp8 path must give exactly the float path's results on them."""
+    latent, q, idx, bt, lens, P, Dl = _fp8_case(21)
+    qs, ks = 2.0 ** -5, 2.0 ** -3
+    lat_f = (oracle.decode_e4m3fn(latent) * ks).astype(np.float32)
+    q_f = (oracle.decode_e4m3fn(q) * qs).astype(np.float32)
+    a = sparse_mla(q, latent, idx, bt, lens, None, P, Dl, 0.11, "fp8", q_scale=qs, kv_scale=ks)
+    b = sparse_mla(q_f, lat_f, idx, bt, lens, None, P, Dl, 0.11, "f32")
+    for t in a:
+        assert np.array_equal(a[t][0], b[t][0]) and np.array_equal(a[t][1], b[t][1])
+
+
+def test_fp8_scale_invariances():
+    """Only scale * q_scale * kv_scale reaches the scores and only kv_scale the
+    values: moving a factor between the scales leaves lse alone and scales
+    the output by what moved into kv_scale."""
+    latent, q, idx, bt, lens, P, Dl = _fp8_case(22)
+    base = sparse_mla(q, latent, idx, bt, lens, None, P, Dl, 0.05, "fp8", q_scale=0.02, kv_scale=0.3)
+    kvx = sparse_mla(q, latent, idx, bt, lens, None, P, Dl, 0.05 / 3.0, "fp8", q_scale=0.02, kv_scale=0.9)
+    qx = sparse_mla(q, latent, idx, bt, lens, None, P, Dl, 0.05 / 7.0, "fp8", q_scale=0.14, kv_scale=0.3)
+    for t in base:
+        np.testing.assert_allclose(kvx[t][0], 3.0 * base[t][0], rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(kvx[t][1], base[t][1], rtol=1e-12)
+        np.testing.assert_allclose(qx[t][0], base[t][0], rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(qx[t][1], base[t][1], rtol=1e-12)
