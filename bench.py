@@ -45,9 +45,10 @@ def algorithmic_work(wl):
     topk_bytes = int(vis.sum()) * 4 + len(vis) * 4 * k
     sel = np.minimum(vis, k)
     Hm, Dl, Dr = cfg.mla_heads, cfg.d_latent, cfg.d_rope
-    msize = 2 if cfg.mla_kind == "bf16" else 4
+    msize = {"bf16": 2, "fp8": 1}.get(cfg.mla_kind, 4)          # cached row and query element
+    osize = 4 if cfg.mla_kind == "f32" else 2                    # output element (bf16 for fp8 too)
     row_bytes = (Dl + Dr) * msize
-    mla_bytes = int(sel.sum()) * row_bytes + len(vis) * (Hm * (Dl + Dr) * msize + Hm * Dl * msize
+    mla_bytes = int(sel.sum()) * row_bytes + len(vis) * (Hm * (Dl + Dr) * msize + Hm * Dl * osize
                                                          + 4 * k + 4 * Hm)
     mla_flops = int(sel.sum()) * Hm * (2 * (Dl + Dr) + 2 * Dl)
     return {
@@ -56,7 +57,7 @@ def algorithmic_work(wl):
         "topk": {"bytes": topk_bytes, "flops": 0, "per_unit": f"4 B per visible score (+{4 * k} B per row)",
                  "units": int(vis.sum())},
         "sparse_mla": {"bytes": mla_bytes, "flops": mla_flops,
-                       "per_unit": f"{row_bytes} B per selected row (+{Hm * (Dl + Dr) * msize + Hm * Dl * msize + 4 * k + 4 * Hm} B per query row)",
+                       "per_unit": f"{row_bytes} B per selected row (+{Hm * (Dl + Dr) * msize + Hm * Dl * osize + 4 * k + 4 * Hm} B per query row)",
                        "units": int(sel.sum())},
     }
 
@@ -283,8 +284,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "dtype_detail": "indexer fp8 e4m3 MFMA with fp32 accumulate; attention bf16 MFMA with fp32 softmax",
+        "dtype": "bf16" if cfg.mla_kind != "fp8" else "fp8+bf16",
+        "dtype_detail": ("indexer fp8 e4m3 MFMA with fp32 accumulate; attention bf16 MFMA with fp32 softmax"
+                         if cfg.mla_kind != "fp8" else
+                         "indexer fp8 e4m3 MFMA; attention scores fp8 e4m3 MFMA, P.V bf16 MFMA (cache codes "
+                         "converted exactly), fp32 accumulate and softmax"),
         "data": "synthetic",
         "launch": "eager" if args.no_graph else "hip graph of the timed steps",
         "config": {"workload": cfg.name, "description": cfg.note, "batch": cfg.batch,

@@ -80,6 +80,9 @@ CONFIGS = {
                                 note="chunked prefill: 4096 rows on a 16384 prefix"),
     "decode_b64_32k": Config("decode_b64_32k", seed=5, batch=64, ctx=(32768,) * 64,
                              note="batch-64 decode, every ctx 32768"),
+    "decode_b64_ragged_fp8": Config("decode_b64_ragged_fp8", seed=2, batch=64, ctx_range=(4096, 32768),
+                                    mla_kind="fp8",
+                                    note="ragged batch-64 decode over an fp8 latent cache (per-tensor scales)"),
     "mtp_b64x2_ragged": Config("mtp_b64x2_ragged", seed=2, batch=64, ctx_range=(4096, 32768),
                                q_lens=(2,) * 64,
                                note="multi-token decode, next_n 2, ragged batch 64, ctx U[4096, 32768]"),
@@ -135,6 +138,23 @@ def _to_e4m3fn_bytes(x32):
 
 
 _THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _per_tensor_e4m3(bits16, rows=4096):
+    """E4M3 codes of a bf16 array with one fp32 scale (absmax / 448) for all of it."""
+    flat = bits16.reshape(bits16.shape[0], -1)
+    starts = list(range(0, flat.shape[0], rows))
+    with ThreadPoolExecutor(_THREADS) as ex:
+        amax = max(ex.map(lambda s: float(np.abs(_bf16_bits_to_f32(flat[s:s + rows])).max()), starts))
+    scale = np.float32(max(amax, 1e-30) / F8_MAX)
+    codes = np.empty(flat.shape, dtype=np.uint8)
+
+    def work(s):
+        codes[s:s + rows] = _to_e4m3fn_bytes(_bf16_bits_to_f32(flat[s:s + rows]) / scale)
+
+    with ThreadPoolExecutor(_THREADS) as ex:
+        list(ex.map(work, starts))
+    return codes.reshape(bits16.shape), float(scale)
 
 
 def _fill(shape, seed, array_id, chunk_rows, dtype, convert=lambda x: x):
@@ -259,11 +279,23 @@ def generate(cfg, with_mla=True, with_indexer=True):
     # 6. latent cache, 7. MLA queries
     Dqk = cfg.d_latent + cfg.d_rope
     Hm = cfg.mla_heads
+    extras = {}
     if with_mla:
         if cfg.mla_kind == "bf16":
             latent = _fill((num_pages, P, Dqk), cfg.seed, 4, 128, np.uint16, _to_bf16_bits)
             poison_slots(latent, NAN_BF16)
             q_mla = _fill((T, Hm, Dqk), cfg.seed, 5, 64, np.uint16, _to_bf16_bits)
+        elif cfg.mla_kind == "fp8":
+            # the bf16 rows and queries of the bf16 workload, quantized with
+            # one scale per tensor (absmax / 448 over the live rows)
+            lat16 = _fill((num_pages, P, Dqk), cfg.seed, 4, 128, np.uint16, _to_bf16_bits)
+            poison_slots(lat16, 0)
+            q16 = _fill((T, Hm, Dqk), cfg.seed, 5, 64, np.uint16, _to_bf16_bits)
+            latent, kv_scale = _per_tensor_e4m3(lat16)
+            q_mla, q_scale = _per_tensor_e4m3(q16)
+            del lat16, q16
+            poison_slots(latent, NAN_F8)
+            extras = {"q_scale": q_scale, "kv_scale": kv_scale}
         else:
             latent = _fill((num_pages, P, Dqk), cfg.seed, 4, 128, np.float32)
             poison_slots(latent, np.nan)
@@ -274,7 +306,7 @@ def generate(cfg, with_mla=True, with_indexer=True):
 
     return Workload(cfg=cfg, seq_lens_k=lens.astype(np.int32), cu_seqlens_q=cu,
                     block_table=block_table, num_pages=num_pages, index_cache=cache,
-                    q_idx=q_idx, w=w, latent=latent, q_mla=q_mla)
+                    q_idx=q_idx, w=w, latent=latent, q_mla=q_mla, extras=extras)
 
 
 def small_config(name, seed, lens, q_lens=(), page_size=64, topk=2048, idx_kind="fp8",

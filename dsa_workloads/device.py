@@ -34,4 +34,5 @@ def make_step(wl, device="cuda"):
                    max_seq_len_k=wl.max_seq_len_k, max_seq_len_q=wl.max_seq_len_q,
                    num_rows=wl.num_rows, q_idx=d["q_idx"], w=d["w"], index_cache=d["index_cache"],
                    q_mla=d["q_mla"], kv_cache=d["kv_cache"], topk=cfg.topk,
-                   softmax_scale=cfg.softmax_scale, d_latent=cfg.d_latent)
+                   softmax_scale=cfg.softmax_scale, d_latent=cfg.d_latent,
+                   mla_scales=(wl.extras["q_scale"], wl.extras["kv_scale"]) if cfg.mla_kind == "fp8" else None)

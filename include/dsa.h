@@ -13,6 +13,10 @@
  *   dsa_quant_index_q   fp8 index queries, per-head scale folded into the gates
  *   dsa_store_index_k   fp8 quantization of new index keys + their paged store
  *
+ * and the attention over an fp8 latent cache:
+ *
+ *   sparse_mla_decode_fp8, sparse_mla_prefill_fp8
+ *
  * Sources: the SGLang "dsa_indexer.py" page (Indexer._get_topk_paged calls the
  * paged fp8 MQA-logits kernel with q_fp8 [T,H,128], the 132-byte-per-token
  * index cache, weights [T,H], seqlens and block tables, then topk_transform),
@@ -212,7 +216,8 @@ dsa_status_t dsa_topk(const dsa_batch_t *batch,
  * kv_cache: [num_pages, P, d_latent + d_rope]
  * dtype:    BF16 with (Hm, d_latent, d_rope) = (128, 512, 64) or any Hm that is
  *           a multiple of 64 with those dims; or F32 with Hm <= 128,
- *           d_latent + d_rope <= 1024, d_latent <= 512.
+ *           d_latent + d_rope <= 1024, d_latent <= 512. (An fp8 cache goes
+ *           through sparse_mla_*_fp8; FP8_E4M3 here is UNSUPPORTED.)
  * topk_idx: [T, k] int32, 1 <= k <= 4096.
  * out:      [T, Hm, d_latent] in dtype.   lse: [T, Hm] fp32, may be NULL.
  * workspace: at least dsa_workspace_bytes(DSA_OP_MLA_DECODE or _PREFILL, ...)
@@ -240,11 +245,52 @@ dsa_status_t sparse_mla_prefill(const dsa_batch_t *batch,
                                 dsa_stream_t stream);
 
 /*
+ * sparse_mla_decode_fp8 / sparse_mla_prefill_fp8 - the same attention over an
+ * fp8 latent cache (vLLM MLA page, the decode path under fp8_attention: the
+ * absorbed query and its rope part quantized with the layer's q scale by
+ * scaled_fp8_quant, the cache written in fp8 with the layer's k scale). q and
+ * kv_cache hold OCP E4M3 codes, one scale per tensor:
+ *
+ *   z_i        = softmax_scale * q_scale * kv_scale * (q8[t,h,:] . C8_i)
+ *   out[t,h,:] = kv_scale * sum_i softmax(z)_i * C8_i[:512]
+ *   lse[t,h]   = log(sum_i exp(z_i))                  (natural log)
+ *
+ * with the entry rules of sparse_mla_decode (invalid entries skipped, empty
+ * selection -> out 0 and lse -inf).
+ * q:        [T, Hm, 576] codes (512 latent, then 64 rope), 16-byte aligned rows.
+ * kv_cache: [num_pages, P, 576] codes (576 bytes per cached row).
+ * Hm a multiple of 64, d_latent 512, d_rope 64; q_scale, kv_scale finite, > 0.
+ * out:      [T, Hm, 512] bf16.   lse: [T, Hm] fp32, may be NULL.
+ * workspace: at least dsa_workspace_bytes(DSA_OP_MLA_DECODE or _PREFILL, ...,
+ *           DSA_FP8_E4M3) bytes (split partials; always at least two splits
+ *           when k > 1024); NULL if that is 0.
+ */
+dsa_status_t sparse_mla_decode_fp8(const dsa_batch_t *batch,
+                                   const void *q, float q_scale,
+                                   const void *kv_cache, float kv_scale,
+                                   const int32_t *topk_idx, int32_t k,
+                                   int32_t num_heads, int32_t d_latent, int32_t d_rope,
+                                   float softmax_scale,
+                                   void *out, float *lse,
+                                   void *workspace, size_t workspace_bytes,
+                                   dsa_stream_t stream);
+
+dsa_status_t sparse_mla_prefill_fp8(const dsa_batch_t *batch,
+                                    const void *q, float q_scale,
+                                    const void *kv_cache, float kv_scale,
+                                    const int32_t *topk_idx, int32_t k,
+                                    int32_t num_heads, int32_t d_latent, int32_t d_rope,
+                                    float softmax_scale,
+                                    void *out, float *lse,
+                                    void *workspace, size_t workspace_bytes,
+                                    dsa_stream_t stream);
+
+/*
  * dsa_workspace_bytes - device workspace an op needs for this batch (host-only,
  * launches nothing). Returns 0 for an op that needs none, and (size_t)-1 when
  * the arguments are invalid (dsa_last_error() says why). `num_heads` and
  * `d_latent` are the MLA ones; they are ignored for DSA_OP_TOPK. `dtype` is the
- * MLA dtype.
+ * MLA dtype (DSA_FP8_E4M3 for the sparse_mla_*_fp8 calls).
  */
 size_t dsa_workspace_bytes(dsa_op_t op, const dsa_batch_t *batch, int32_t k,
                            int32_t num_heads, int32_t d_latent, dsa_dtype_t dtype);

@@ -18,7 +18,8 @@ __all__ = [
     "DSA_OK", "DSA_F32", "DSA_BF16", "DSA_FP8_E4M3", "DSA_OP_TOPK", "DSA_OP_MLA_DECODE",
     "DSA_OP_MLA_PREFILL", "DsaError", "DsaBatch", "lib", "library_path", "make_batch",
     "dsa_indexer_logits", "dsa_topk", "sparse_mla_decode", "sparse_mla_prefill",
-    "dsa_quant_index_q", "dsa_store_index_k", "dsa_workspace_bytes", "dsa_version", "EXPORTED_SYMBOLS",
+    "dsa_quant_index_q", "dsa_store_index_k", "sparse_mla_decode_fp8", "sparse_mla_prefill_fp8",
+    "dsa_workspace_bytes", "dsa_version", "EXPORTED_SYMBOLS",
 ]
 
 DSA_OK, DSA_ERR_INVALID_ARGUMENT, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE_TOO_SMALL, DSA_ERR_HIP = range(5)
@@ -27,7 +28,7 @@ DSA_OP_TOPK, DSA_OP_MLA_DECODE, DSA_OP_MLA_PREFILL = range(3)
 
 EXPORTED_SYMBOLS = (
     "dsa_indexer_logits", "dsa_topk", "sparse_mla_decode", "sparse_mla_prefill",
-    "dsa_quant_index_q", "dsa_store_index_k",
+    "dsa_quant_index_q", "dsa_store_index_k", "sparse_mla_decode_fp8", "sparse_mla_prefill_fp8",
     "dsa_workspace_bytes", "dsa_status_string", "dsa_last_error", "dsa_version",
 )
 
@@ -81,6 +82,10 @@ def lib():
     for name in ("sparse_mla_decode", "sparse_mla_prefill"):
         f = getattr(L, name)
         f.argtypes = [P, V, V, I32, V, I32, I32, I32, I32, F32, V, V, V, SZ, V]
+        f.restype = I32
+    for name in ("sparse_mla_decode_fp8", "sparse_mla_prefill_fp8"):
+        f = getattr(L, name)
+        f.argtypes = [P, V, F32, V, F32, V, I32, I32, I32, I32, F32, V, V, V, SZ, V]
         f.restype = I32
     L.dsa_quant_index_q.argtypes = [V, V, I32, I32, I32, V, V, V]
     L.dsa_quant_index_q.restype = I32
@@ -188,6 +193,29 @@ def sparse_mla_prefill(batch, q, kv_cache, topk_idx, softmax_scale, out, lse=Non
                        *, d_latent=None, stream=None):
     _mla(lib().sparse_mla_prefill, batch, q, kv_cache, topk_idx, softmax_scale, out, lse, workspace,
          d_latent, stream)
+
+
+def _mla_fp8(fn, batch, q, q_scale, kv_cache, kv_scale, topk_idx, softmax_scale, out, lse, workspace, stream):
+    Hm, Dqk = int(q.shape[1]), int(q.shape[2])
+    Dl = int(out.shape[2])
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(fn(batch.ref(), _ptr(q), float(q_scale), _ptr(kv_cache), float(kv_scale), _ptr(topk_idx),
+              int(topk_idx.shape[1]), Hm, Dl, Dqk - Dl, float(softmax_scale), _ptr(out), _ptr(lse),
+              _ptr(workspace), nbytes, _stream(stream)))
+
+
+def sparse_mla_decode_fp8(batch, q, q_scale, kv_cache, kv_scale, topk_idx, softmax_scale, out, lse=None,
+                          workspace=None, *, stream=None):
+    """Sparse MLA over an fp8 latent cache: q, kv_cache E4M3 codes (uint8) with
+    per-tensor scales; out [T, Hm, 512] bf16."""
+    _mla_fp8(lib().sparse_mla_decode_fp8, batch, q, q_scale, kv_cache, kv_scale, topk_idx, softmax_scale,
+             out, lse, workspace, stream)
+
+
+def sparse_mla_prefill_fp8(batch, q, q_scale, kv_cache, kv_scale, topk_idx, softmax_scale, out, lse=None,
+                           workspace=None, *, stream=None):
+    _mla_fp8(lib().sparse_mla_prefill_fp8, batch, q, q_scale, kv_cache, kv_scale, topk_idx, softmax_scale,
+             out, lse, workspace, stream)
 
 
 def dsa_quant_index_q(q, w, q8, w_eff, stream=None):

@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
 
-SOURCES = ["dsa_api.cpp", "indexer.hip", "topk.hip", "sparse_mla.hip", "quant.hip"]
+SOURCES = ["dsa_api.cpp", "indexer.hip", "topk.hip", "sparse_mla.hip", "sparse_mla_fp8.hip", "quant.hip"]
 
 ARCH = os.environ.get("DSA_OFFLOAD_ARCH", "gfx950")
 
@@ -36,6 +36,8 @@ COMMON_FLAGS = [
 SOURCE_FLAGS = {
     "sparse_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1",
                        "-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
+    "sparse_mla_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1",
+                           "-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
     "indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 

@@ -79,6 +79,7 @@ dsa_status_t check_batch(const dsa_batch_t* batch, BatchView* bv) {
 
 struct MlaPlan {
   bool bf16;
+  bool fp8;
   int splits;
   int entries_per_split;
   size_t workspace;
@@ -89,13 +90,16 @@ dsa_status_t plan_mla(const BatchView& bv, int32_t k, int32_t num_heads, int32_t
   if (k < 1 || k > kTopkMaxK) return fail(DSA_ERR_INVALID_ARGUMENT, "k %d outside [1, %d]", k, kTopkMaxK);
   if (num_heads < 1 || d_latent < 1 || d_rope < 0)
     return fail(DSA_ERR_INVALID_ARGUMENT, "num_heads %d, d_latent %d, d_rope %d", num_heads, d_latent, d_rope);
-  if (dtype == DSA_BF16) {
+  plan->fp8 = false;
+  if (dtype == DSA_BF16 || dtype == DSA_FP8_E4M3) {
     if (d_latent != kMlaDl || d_rope != kMlaDr || num_heads % kMlaHeadsPerGroup != 0)
       return fail(DSA_ERR_UNSUPPORTED,
-                  "bf16 sparse MLA needs d_latent 512, d_rope 64 and a multiple of 64 heads "
-                  "(got %d, %d, %d)", d_latent, d_rope, num_heads);
-    plan->bf16 = true;
-    plan->splits = mla_bf16_splits(bv.num_rows, k, num_heads);
+                  "%s sparse MLA needs d_latent 512, d_rope 64 and a multiple of 64 heads "
+                  "(got %d, %d, %d)", dtype == DSA_BF16 ? "bf16" : "fp8", d_latent, d_rope, num_heads);
+    plan->bf16 = dtype == DSA_BF16;
+    plan->fp8 = dtype == DSA_FP8_E4M3;
+    plan->splits = plan->fp8 ? mla_fp8_splits(bv.num_rows, k, num_heads)
+                             : mla_bf16_splits(bv.num_rows, k, num_heads);
     plan->entries_per_split = mla_entries_per_split(k, plan->splits);
     plan->workspace = 0;
     if (plan->splits > 1) {
@@ -106,6 +110,7 @@ dsa_status_t plan_mla(const BatchView& bv, int32_t k, int32_t num_heads, int32_t
     return ok();
   }
   if (dtype == DSA_F32) {
+    plan->fp8 = false;
     if (num_heads > 128 || d_latent > 512 || d_latent + d_rope > 1024)
       return fail(DSA_ERR_UNSUPPORTED, "f32 sparse MLA supports num_heads <= 128, d_latent <= 512, "
                   "d_latent + d_rope <= 1024 (got %d, %d, %d)", num_heads, d_latent, d_rope);
@@ -121,7 +126,8 @@ dsa_status_t plan_mla(const BatchView& bv, int32_t k, int32_t num_heads, int32_t
 dsa_status_t run_mla(const dsa_batch_t* batch, bool decode, const void* q, const void* kv_cache,
                      dsa_dtype_t dtype, const int32_t* topk_idx, int32_t k, int32_t num_heads,
                      int32_t d_latent, int32_t d_rope, float softmax_scale, void* out, float* lse,
-                     void* workspace, size_t workspace_bytes, dsa_stream_t stream) {
+                     void* workspace, size_t workspace_bytes, dsa_stream_t stream,
+                     float q_scale = 1.f, float kv_scale = 1.f) {
   BatchView bv;
   dsa_status_t st = check_batch(batch, &bv);
   if (st != DSA_OK) return st;
@@ -134,6 +140,8 @@ dsa_status_t run_mla(const dsa_batch_t* batch, bool decode, const void* q, const
   if (st != DSA_OK) return st;
   if (!(softmax_scale == softmax_scale) || softmax_scale == INFINITY || softmax_scale == -INFINITY)
     return fail(DSA_ERR_INVALID_ARGUMENT, "softmax_scale is not finite");
+  if (!(q_scale > 0.f && q_scale < INFINITY && kv_scale > 0.f && kv_scale < INFINITY))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "q_scale / kv_scale must be finite and positive");
   if (bv.num_rows > 0 && (!q || !kv_cache || !topk_idx || !out))
     return fail(DSA_ERR_INVALID_ARGUMENT, "q / kv_cache / topk_idx / out is NULL");
   if (workspace_bytes < plan.workspace)
@@ -152,6 +160,8 @@ dsa_status_t run_mla(const dsa_batch_t* batch, bool decode, const void* q, const
   p.d_latent = d_latent;
   p.d_rope = d_rope;
   p.softmax_scale = softmax_scale;
+  p.q_scale = q_scale;
+  p.kv_scale = kv_scale;
   p.out = out;
   p.lse = lse;
   p.splits = plan.splits;
@@ -164,7 +174,8 @@ dsa_status_t run_mla(const dsa_batch_t* batch, bool decode, const void* q, const
     p.part_lse = reinterpret_cast<float*>(static_cast<uint16_t*>(workspace) + parts * (size_t)d_latent);
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  return from_hip(plan.bf16 ? launch_mla_bf16(p, s) : launch_mla_f32(p, s), "sparse MLA launch");
+  return from_hip(plan.fp8 ? launch_mla_fp8(p, s) : plan.bf16 ? launch_mla_bf16(p, s) : launch_mla_f32(p, s),
+                  "sparse MLA launch");
 }
 
 }  // namespace
@@ -290,6 +301,8 @@ dsa_status_t sparse_mla_decode(const dsa_batch_t* batch, const void* q, const vo
                                int32_t num_heads, int32_t d_latent, int32_t d_rope, float softmax_scale,
                                void* out, float* lse, void* workspace, size_t workspace_bytes,
                                dsa_stream_t stream) {
+  if (dtype == DSA_FP8_E4M3)
+    return fail(DSA_ERR_UNSUPPORTED, "an fp8 latent cache goes through sparse_mla_decode_fp8 (it needs the scales)");
   return run_mla(batch, true, q, kv_cache, dtype, topk_idx, k, num_heads, d_latent, d_rope,
                  softmax_scale, out, lse, workspace, workspace_bytes, stream);
 }
@@ -299,8 +312,26 @@ dsa_status_t sparse_mla_prefill(const dsa_batch_t* batch, const void* q, const v
                                 int32_t num_heads, int32_t d_latent, int32_t d_rope, float softmax_scale,
                                 void* out, float* lse, void* workspace, size_t workspace_bytes,
                                 dsa_stream_t stream) {
+  if (dtype == DSA_FP8_E4M3)
+    return fail(DSA_ERR_UNSUPPORTED, "an fp8 latent cache goes through sparse_mla_prefill_fp8 (it needs the scales)");
   return run_mla(batch, false, q, kv_cache, dtype, topk_idx, k, num_heads, d_latent, d_rope,
                  softmax_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+dsa_status_t sparse_mla_decode_fp8(const dsa_batch_t* batch, const void* q, float q_scale, const void* kv_cache,
+                                   float kv_scale, const int32_t* topk_idx, int32_t k, int32_t num_heads,
+                                   int32_t d_latent, int32_t d_rope, float softmax_scale, void* out, float* lse,
+                                   void* workspace, size_t workspace_bytes, dsa_stream_t stream) {
+  return run_mla(batch, true, q, kv_cache, DSA_FP8_E4M3, topk_idx, k, num_heads, d_latent, d_rope,
+                 softmax_scale, out, lse, workspace, workspace_bytes, stream, q_scale, kv_scale);
+}
+
+dsa_status_t sparse_mla_prefill_fp8(const dsa_batch_t* batch, const void* q, float q_scale, const void* kv_cache,
+                                    float kv_scale, const int32_t* topk_idx, int32_t k, int32_t num_heads,
+                                    int32_t d_latent, int32_t d_rope, float softmax_scale, void* out, float* lse,
+                                    void* workspace, size_t workspace_bytes, dsa_stream_t stream) {
+  return run_mla(batch, false, q, kv_cache, DSA_FP8_E4M3, topk_idx, k, num_heads, d_latent, d_rope,
+                 softmax_scale, out, lse, workspace, workspace_bytes, stream, q_scale, kv_scale);
 }
 
 size_t dsa_workspace_bytes(dsa_op_t op, const dsa_batch_t* batch, int32_t k, int32_t num_heads,
@@ -316,7 +347,7 @@ size_t dsa_workspace_bytes(dsa_op_t op, const dsa_batch_t* batch, int32_t k, int
   }
   if (op == DSA_OP_MLA_DECODE || op == DSA_OP_MLA_PREFILL) {
     MlaPlan plan;
-    const int d_rope = dtype == DSA_BF16 ? kMlaDr : 0;
+    const int d_rope = (dtype == DSA_BF16 || dtype == DSA_FP8_E4M3) ? kMlaDr : 0;
     if (plan_mla(bv, k, num_heads, d_latent, d_rope, dtype, &plan) != DSA_OK) return (size_t)-1;
     return plan.workspace;
   }

@@ -55,6 +55,8 @@ struct MlaParams {
   int32_t d_latent;
   int32_t d_rope;
   float softmax_scale;
+  float q_scale;          // fp8 path: q = codes * q_scale, rows = codes * kv_scale
+  float kv_scale;
   void* out;              // [T, Hm, Dl]
   float* lse;             // [T, Hm] or nullptr
   // split-KV partials (splits > 1): O / l as [T, splits, Hm, Dl] bf16 bits and
@@ -74,6 +76,7 @@ constexpr int kMlaDr = 64;
 constexpr int kMlaDqk = kMlaDl + kMlaDr;
 constexpr int kMlaTile = 32;
 constexpr int kMlaMaxEntriesPerBlock = 2048;
+constexpr int kMlaFp8MaxEntriesPerBlock = 1024;
 constexpr int kTopkMaxK = 4096;
 
 // Split-KV policy for the bf16 kernel: enough work-groups to cover the chip
@@ -113,5 +116,8 @@ hipError_t launch_indexer_f32(const IndexerParams& p, hipStream_t s);
 hipError_t launch_topk(const TopkParams& p, hipStream_t s);
 hipError_t launch_mla_bf16(const MlaParams& p, hipStream_t s);
 hipError_t launch_mla_f32(const MlaParams& p, hipStream_t s);
+hipError_t launch_mla_fp8(const MlaParams& p, hipStream_t s);
+hipError_t launch_mla_combine_bf16(const MlaParams& p, hipStream_t s);
+int mla_fp8_splits(int num_rows, int k, int heads);
 
 }  // namespace dsa

@@ -648,8 +648,27 @@ hipError_t launch_mla_bf16(const MlaParams& p, hipStream_t s) {
   hipLaunchKernelGGL(mla_bf16_kernel, dim3((unsigned)blocks), dim3(kMlaThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  hipLaunchKernelGGL(mla_combine_kernel<true>, dim3(T, (p.heads + 1) / 2), dim3(256), 0, s, p);
+  return launch_mla_combine_bf16(p, s);
+}
+
+hipError_t launch_mla_combine_bf16(const MlaParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(mla_combine_kernel<true>, dim3(p.batch.num_rows, (p.heads + 1) / 2), dim3(256), 0, s, p);
   return hipGetLastError();
+}
+
+// Splits of the fp8 kernel: as for bf16, with at most 1024 entries per split
+// (its compacted row ids take 4 KB of LDS) and at least two 64-row tiles.
+int mla_fp8_splits(int num_rows, int k, int heads) {
+  const int groups = num_rows * (heads / kMlaHeadsPerGroup);
+  const int min_splits = (k + kMlaFp8MaxEntriesPerBlock - 1) / kMlaFp8MaxEntriesPerBlock;
+  if (groups <= 0) return min_splits < 1 ? 1 : min_splits;
+  int max_splits = (k + 128 - 1) / 128;
+  if (max_splits > 16) max_splits = 16;
+  int sp = (256 + groups - 1) / groups;
+  if (sp > max_splits) sp = max_splits;
+  if (sp < min_splits) sp = min_splits;
+  if (sp < 1) sp = 1;
+  return sp;
 }
 
 hipError_t launch_mla_f32(const MlaParams& p, hipStream_t s) {

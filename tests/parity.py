@@ -91,7 +91,8 @@ def check_topk_near_ties(gpu_idx_row, ref_logits_row, visible, k):
 def check_attention(gpu_out, gpu_lse, wl, gpu_idx, rows, fp32=False):
     res = oracle.sparse_mla(wl.q_mla, wl.latent, gpu_idx, wl.block_table, wl.seq_lens_k,
                             wl.cu_seqlens_q, wl.cfg.page_size, wl.cfg.d_latent,
-                            wl.cfg.softmax_scale, wl.cfg.mla_kind, rows=rows)
+                            wl.cfg.softmax_scale, wl.cfg.mla_kind, rows=rows,
+                            q_scale=wl.extras.get("q_scale", 1.0), kv_scale=wl.extras.get("kv_scale", 1.0))
     atol, rtol = (1e-4, 1e-4) if fp32 else (2e-2, 1e-2)
     latol, lrtol = (1e-5, 1e-5) if fp32 else (1e-3, 1e-3)
     worst = 0.0

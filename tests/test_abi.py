@@ -203,3 +203,23 @@ def test_quant_entry_points_validate_on_the_host(L):
     assert L.dsa_store_index_k(V(0x100), 3, 128, None, 64, 4, V(0x300), None) == dsa.DSA_ERR_INVALID_ARGUMENT
     assert L.dsa_store_index_k(V(0x100), 3, 128, V(0x200), 64, 4, V(0x308), None) == \
         dsa.DSA_ERR_INVALID_ARGUMENT                                                 # cache misaligned
+
+
+def test_fp8_attention_entry_points_validate_on_the_host(L):
+    b = _batch()
+    V = ctypes.c_void_p
+
+    def call(q_scale=0.02, kv_scale=0.01, H=128, Dl=512, Dr=64, ws=None, wsb=0):
+        return L.sparse_mla_decode_fp8(ctypes.byref(b), V(0x10), q_scale, V(0x20), kv_scale, V(0x30), 2048,
+                                       H, Dl, Dr, 0.07, V(0x40), None, ws, wsb, None)
+    need = L.dsa_workspace_bytes(dsa.DSA_OP_MLA_DECODE, ctypes.byref(b), 2048, 128, 512, dsa.DSA_FP8_E4M3)
+    rows = b.num_rows
+    assert need >= rows * 2 * 128 * (512 * 2 + 4)                      # at least two splits
+    assert call(q_scale=0.0, ws=V(0x1000), wsb=need) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert call(kv_scale=float("inf"), ws=V(0x1000), wsb=need) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert call(H=96, ws=V(0x1000), wsb=need) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(Dr=32, ws=V(0x1000), wsb=need) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(ws=V(0x1000), wsb=need - 1) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
+    # the plain entry point does not take an fp8 cache (it has no scales)
+    assert L.sparse_mla_decode(ctypes.byref(b), V(0x10), V(0x20), dsa.DSA_FP8_E4M3, V(0x30), 2048, 128, 512, 64,
+                               0.07, V(0x40), None, V(0x1000), need, None) == dsa.DSA_ERR_UNSUPPORTED

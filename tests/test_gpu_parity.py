@@ -73,6 +73,11 @@ SMALL = [
     small_config("mtp_x4_p16", seed=112, lens=[700, 4100, 2047], q_lens=[4, 4, 4], page_size=16,
                  topk=512),
     small_config("mtp_x3_short", seed=113, lens=[3, 2050, 64], q_lens=[3, 3, 3], topk=2048),
+    # fp8 latent cache (per-tensor query and cache scales)
+    small_config("dec3_fp8", seed=114, lens=[100, 2100, 5000], mla_kind="fp8"),
+    small_config("pre2_fp8", seed=115, lens=[300, 2500], q_lens=[37, 64], mla_kind="fp8"),
+    small_config("dec_fp8_k4096", seed=116, lens=[5000, 4097], topk=4096, mla_kind="fp8"),
+    small_config("dec_fp8_empty_p16", seed=117, lens=[0, 700, 65], page_size=16, topk=256, mla_kind="fp8"),
 ]
 
 
@@ -103,6 +108,14 @@ def test_full_multi_token_decode_sampled():
     lens = wl.seq_lens_k
     b_min, b_max = int(np.argmin(lens)), int(np.argmax(lens))
     rows = sorted({2 * b_min, 2 * b_min + 1, 2 * b_max, 2 * b_max + 1, 35})
+    _full_check(cfg, rows=rows)
+
+
+def test_full_ragged_batch64_fp8_cache_sampled():
+    cfg = CONFIGS["decode_b64_ragged_fp8"]
+    wl = generate(cfg, with_mla=False)
+    lens = wl.seq_lens_k
+    rows = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 40})
     _full_check(cfg, rows=rows)
 
 
