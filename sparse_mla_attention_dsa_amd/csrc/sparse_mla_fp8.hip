@@ -23,10 +23,13 @@
 //     which converts exactly to bf16 (v_cvt_scalef32_pk_bf16_fp8) and feeds
 //     the bf16 MFMA with P^T as B, so P stays bf16 as in the bf16 kernel.
 // Swizzle: inside row r the 16-byte chunk q sits at chunk q ^ ((r >> 2) & 3)
-// (rows are 576 bytes = 144 banks apart, 16 mod 64): the score reads (16 rows,
-// one chunk each) and the transposing value reads (8 rows x 16 bytes per
-// 16-lane block) then touch distinct banks. P rows are padded to 72 elements
-// for the same reason.
+// (rows are 576 bytes apart). With it the transposing value reads (8 rows x
+// 16 bytes per 16-lane block) run at ~234 B/clk per CU and the score reads at
+// ~246 B/clk, the latter only because the sixteen M indices of a score row
+// block are the tile rows k and k + 8 side by side (measured on gfx950 by a
+// search over chunk swizzles and row orders: no swizzle serves both read
+// patterns with the plain row order). P rows are padded to 72 elements so that
+// the P^T reads of sixteen heads fall on distinct banks.
 #include "device_common.h"
 #include "dsa_internal.h"
 
@@ -269,14 +272,19 @@ __global__ __launch_bounds__(kF8Threads) void mla_fp8_kernel(MlaParams p) {
     float m_ref = -INFINITY;
     float l_part = 0.f;
 
-    // row operand (A) of block kb: lane (c, g) reads row 16 rb + c, logical
-    // chunks 8 kb + 2 g and + 1 (the rope block: chunks 32 + 2 (g & 1), + 1,
-    // zeroed for g >= 2 after the read, so every address stays in its row)
+    // row operand (A) of block kb: M index c of row block rb is tile row
+    // 16 rb + (c >> 1) + 8 (c & 1) (rows k and k + 8 side by side: with the
+    // chunk swizzle the sixteen 16-byte reads of a quarter wave then fall on
+    // distinct banks, measured on gfx950, where rows 16 rb + c conflict two-way);
+    // lane (c, g) reads logical chunks 8 kb + 2 g and + 1 of it (the rope
+    // block: chunks 32 + 2 (g & 1), + 1, zeroed for g >= 2 after the read, so
+    // every address stays in its row)
     const int lo_chunk = 2 * (g & 1);
+    const int a_row = (c >> 1) + 8 * (c & 1);
     auto read_kb = [&](const uint8_t* kvt, int kb, i32x8 (&dst)[kF8RowBlocks]) {
 #pragma unroll
       for (int rb = 0; rb < kF8RowBlocks; ++rb) {
-        const int row = 16 * rb + c;
+        const int row = 16 * rb + a_row;
         const int q0 = kb < 4 ? 8 * kb + 2 * g : 32 + lo_chunk;
         const uint8_t* base = kvt + row * kF8RowBytes;
         const i32x4 lo = *reinterpret_cast<const i32x4*>(base + ((q0 ^ swz8(row)) << 4));
@@ -286,7 +294,8 @@ __global__ __launch_bounds__(kF8Threads) void mla_fp8_kernel(MlaParams p) {
         dst[rb] = v;
       }
     };
-    // S[rows, head hl_s] of one tile: lane (c, g) ends with rows 16 rb + 4 g + i
+    // S[rows, head hl_s] of one tile: lane (c, g) ends with M indices 4 g + i
+    // of each row block, i.e. tile rows 16 rb + 2 g + (i >> 1) + 8 (i & 1)
     auto scores = [&](const uint8_t* kvt, f32x4 (&sacc)[kF8RowBlocks], int copy_tile, int (&rid)[kF8PiecesMax]) {
       i32x8 op[2][kF8RowBlocks];
 #pragma unroll
@@ -302,9 +311,10 @@ __global__ __launch_bounds__(kF8Threads) void mla_fp8_kernel(MlaParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    // online softmax of one tile: the lane's 16 probabilities as bf16 (rows
-    // 16 rb + 4 g .. + 3 in pa[rb]) and its head's rescale factor
-    auto softmax = [&](int tile, const f32x4 (&sacc)[kF8RowBlocks], bf16x4 (&pa)[kF8RowBlocks], float* alpha) {
+    // online softmax of one tile: the lane's 16 probabilities as bf16 pairs
+    // (pa[rb][0]: tile rows 16 rb + 2 g, + 1; pa[rb][1]: 16 rb + 8 + 2 g, + 1)
+    // and its head's rescale factor
+    auto softmax = [&](int tile, const f32x4 (&sacc)[kF8RowBlocks], bf16x2 (&pa)[kF8RowBlocks][2], float* alpha) {
       const int rows_left = nvalid - tile * kF8Tile;
       float sv[4 * kF8RowBlocks];
       float mx = -INFINITY;
@@ -312,7 +322,8 @@ __global__ __launch_bounds__(kF8Threads) void mla_fp8_kernel(MlaParams p) {
       for (int rb = 0; rb < kF8RowBlocks; ++rb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float v = (16 * rb + 4 * g + i < rows_left) ? sacc[rb][i] * scale_log2 : -INFINITY;
+          const int row = 16 * rb + 2 * g + (i >> 1) + 8 * (i & 1);
+          const float v = (row < rows_left) ? sacc[rb][i] * scale_log2 : -INFINITY;
           sv[4 * rb + i] = v;
           mx = fmaxf(mx, v);
         }
@@ -331,15 +342,16 @@ __global__ __launch_bounds__(kF8Threads) void mla_fp8_kernel(MlaParams p) {
           pr[i] = __builtin_amdgcn_exp2f(sv[4 * rb + i] - m_ref);
           l_part += pr[i];
         }
-        const bf16x2 x = __builtin_convertvector(f32x2{pr[0], pr[1]}, bf16x2);
-        const bf16x2 y = __builtin_convertvector(f32x2{pr[2], pr[3]}, bf16x2);
-        pa[rb] = bf16x4{x[0], x[1], y[0], y[1]};
+        pa[rb][0] = __builtin_convertvector(f32x2{pr[0], pr[2]}, bf16x2);   // rows 2 g, 2 g + 1
+        pa[rb][1] = __builtin_convertvector(f32x2{pr[1], pr[3]}, bf16x2);   // rows 8 + 2 g, 8 + 2 g + 1
       }
     };
-    auto publish = [&](const bf16x4 (&pa)[kF8RowBlocks], float alpha) {   // between B1 and B2
+    auto publish = [&](const bf16x2 (&pa)[kF8RowBlocks][2], float alpha) {   // between B1 and B2
 #pragma unroll
-      for (int rb = 0; rb < kF8RowBlocks; ++rb)
-        *reinterpret_cast<bf16x4*>(&sh.p[hl_s * kF8PStride + 16 * rb + 4 * g]) = pa[rb];
+      for (int rb = 0; rb < kF8RowBlocks; ++rb) {
+        *reinterpret_cast<bf16x2*>(&sh.p[hl_s * kF8PStride + 16 * rb + 2 * g]) = pa[rb][0];
+        *reinterpret_cast<bf16x2*>(&sh.p[hl_s * kF8PStride + 16 * rb + 8 + 2 * g]) = pa[rb][1];
+      }
       if (g == 0) sh.alpha[hl_s] = alpha;
       const bool any = __ballot(alpha != 1.f) != 0ull;
       if (lane == 0) sh.flag[rw] = any ? 1 : 0;
@@ -351,7 +363,7 @@ __global__ __launch_bounds__(kF8Threads) void mla_fp8_kernel(MlaParams p) {
       f32x4 sacc[kF8RowBlocks];
       scores(sh.kv[0], sacc, -1, rid_next);
       float alpha;
-      bf16x4 pa[kF8RowBlocks];
+      bf16x2 pa[kF8RowBlocks][2];
       softmax(0, sacc, pa, &alpha);
       publish(pa, alpha);
       wait_tiles8(min(n_tiles, kAhead) - 2, five);
@@ -359,7 +371,7 @@ __global__ __launch_bounds__(kF8Threads) void mla_fp8_kernel(MlaParams p) {
     }
     for (int tile = 0; tile < n_tiles; ++tile) {
       const bool more = tile + 1 < n_tiles;
-      bf16x4 pa[kF8RowBlocks];
+      bf16x2 pa[kF8RowBlocks][2];
       float alpha = 1.f;
       const int last = n_tiles - 1;
       const int copy_tile = tile + kAhead <= last ? tile + kAhead : -1;
