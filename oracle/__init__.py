@@ -34,6 +34,8 @@ Parity status per function (what pins it; see tests/test_oracle_*.py):
 * dsa.indexer_logits ..................... pinned (hand-worked golden example,
   brute-force loops, textbook matmul special case, page-permutation and
   zero-weight-head invariances).
+* dsa.mask_init_and_local ................ pinned (brute force over small
+  rows, the forced positions always selected, the rest ranked as before).
 * dsa.topk ............................... pinned (brute-force full sort,
   short-row rule, order-statistic property, affine invariance).
 * dsa.sparse_mla ......................... pinned (closed forms for one index
@@ -60,6 +62,7 @@ from .dsa import (  # noqa: F401
     indexer_logits,
     indexer_logits_row,
     lse_merge,
+    mask_init_and_local,
     row_layout,
     sparse_mla,
     sparse_mla_row,

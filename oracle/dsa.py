@@ -100,8 +100,27 @@ def indexer_logits_row(q_row, w_row, keys, sigma):
     return gated @ w_row                            # sum over heads
 
 
+def mask_init_and_local(logits_row, visible, num_init, num_local):
+    """Force the first `num_init` and the last `num_local` visible positions
+    into the selection by giving them +inf (SGLang indexer page,
+    `Indexer._mask_init_and_local_tokens`: +inf is scattered at
+    `row_start + arange(num_init)` and at `length - 1 - arange(num_local)`,
+    clamped to the row). Rows start at position 0 here; positions at or past
+    the visible length are not defined anyway. Returns a new array."""
+    out = np.array(logits_row, dtype=np.float64, copy=True)
+    n = int(visible)
+    for i in range(int(num_init)):
+        if i < n:
+            out[i] = np.inf
+    for i in range(int(num_local)):
+        pos = max(n - 1 - i, 0)
+        if pos < n:
+            out[pos] = np.inf
+    return out
+
+
 def indexer_logits(q, w, index_cache, block_table, seq_lens_k, cu_seqlens_q,
-                   page_size, kind, rows=None):
+                   page_size, kind, rows=None, num_init=0, num_local=0):
     """Logits for every query row (or only the listed `rows`).
 
     q: [T, H, D] fp8 codes (uint8) for kind "fp8", float32 for kind "f32".
@@ -125,6 +144,8 @@ def indexer_logits(q, w, index_cache, block_table, seq_lens_k, cu_seqlens_q,
         q_row = decode_e4m3fn(q[t]) if kind == "fp8" else np.asarray(q[t], dtype=np.float64)
         w_row = np.asarray(w[t], dtype=np.float64)
         out[t] = indexer_logits_row(q_row, w_row, keys[:r.visible], sigma[:r.visible])
+        if num_init or num_local:
+            out[t] = mask_init_and_local(out[t], r.visible, num_init, num_local)
     return out
 
 

@@ -58,3 +58,27 @@ def test_ties_go_to_lower_positions():
     vals = np.zeros(10)
     vals[7] = 1.0
     assert list(topk_row(vals, 10, 3)) == [0, 1, 7]
+
+
+def test_init_and_local_forcing():
+    """Forced positions are the first num_init and the last num_local of the
+    visible row (clamped), set to +inf; top-k then always holds them and ranks
+    the rest by value, as with no forcing."""
+    from oracle import mask_init_and_local, topk_row
+    rng = np.random.default_rng(31)
+    for n, ni, nl, k in [(50, 3, 4, 10), (5, 8, 0, 4), (6, 0, 9, 3), (40, 0, 0, 8), (1, 1, 1, 1), (30, 2, 2, 4)]:
+        row = rng.standard_normal(n)
+        got = mask_init_and_local(row, n, ni, nl)
+        forced = {i for i in range(min(ni, n))} | {max(n - 1 - i, 0) for i in range(nl)}
+        for i in range(n):
+            assert (got[i] == np.inf) == (i in forced), (n, ni, nl, i)
+            if i not in forced:
+                assert got[i] == row[i]
+        sel = topk_row(got, n, k)
+        chosen = set(int(x) for x in sel if x >= 0)
+        if len(forced) <= k:
+            assert forced <= chosen
+            rest = sorted((i for i in range(n) if i not in forced), key=lambda i: (-row[i], i))
+            assert chosen - forced == set(rest[:min(k, n) - len(forced)])
+        else:
+            assert chosen == set(sorted(forced)[:k])       # ties at +inf go to the lower positions
