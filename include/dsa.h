@@ -121,6 +121,11 @@ typedef struct {
  * logits:   [T, logits_row_stride] fp32, logits_row_stride >= max visible.
  *           Columns >= visible(t) are left unwritten (the pages call their kernels
  *           with clean_logits=False); a position whose page is absent gets -inf.
+ * num_init_tokens, num_local_tokens >= 0: init/local-token forcing (SGLang page,
+ *           Indexer._mask_init_and_local_tokens): the positions s < num_init_tokens
+ *           and s >= visible(t) - num_local_tokens of each row (s < visible(t))
+ *           get +inf, so that dsa_topk always selects them (ties at +inf go to
+ *           the lower positions). 0 and 0 turn it off.
  */
 dsa_status_t dsa_indexer_logits(const dsa_batch_t *batch,
                                 const void *q, dsa_dtype_t q_dtype,
@@ -128,6 +133,7 @@ dsa_status_t dsa_indexer_logits(const dsa_batch_t *batch,
                                 const void *index_cache, dsa_dtype_t k_dtype,
                                 int32_t num_heads, int32_t head_dim,
                                 float *logits, int64_t logits_row_stride,
+                                int32_t num_init_tokens, int32_t num_local_tokens,
                                 dsa_stream_t stream);
 
 /*

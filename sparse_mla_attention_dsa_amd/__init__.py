@@ -75,7 +75,7 @@ def lib():
     L = ctypes.CDLL(path)
     P, I32, I64, SZ, F32, V = (ctypes.POINTER(DsaBatch), ctypes.c_int32, ctypes.c_int64,
                                ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p)
-    L.dsa_indexer_logits.argtypes = [P, V, I32, V, V, I32, I32, I32, V, I64, V]
+    L.dsa_indexer_logits.argtypes = [P, V, I32, V, V, I32, I32, I32, V, I64, I32, I32, V]
     L.dsa_indexer_logits.restype = I32
     L.dsa_topk.argtypes = [P, V, I64, I32, V, V, SZ, V]
     L.dsa_topk.restype = I32
@@ -158,13 +158,16 @@ def make_batch(block_table, seq_lens_k, cu_seqlens_q=None, *, page_size, num_pag
     return Batch(s, (block_table, seq_lens_k, cu_seqlens_q))
 
 
-def dsa_indexer_logits(batch, q, w, index_cache, logits, *, num_heads=None, head_dim=None, stream=None):
-    """logits[t, s] = sum_h w[t,h] relu(sigma_s (q[t,h] . k_s)) for s < visible(t)."""
+def dsa_indexer_logits(batch, q, w, index_cache, logits, *, num_heads=None, head_dim=None, num_init_tokens=0,
+                       num_local_tokens=0, stream=None):
+    """logits[t, s] = sum_h w[t,h] relu(sigma_s (q[t,h] . k_s)) for s < visible(t), then +inf at the
+    first num_init_tokens and the last num_local_tokens visible positions of each row."""
     code = _dtype_code(q)
     H = int(q.shape[1]) if num_heads is None else num_heads
     D = int(q.shape[2]) if head_dim is None else head_dim
     _check(lib().dsa_indexer_logits(batch.ref(), _ptr(q), code, _ptr(w), _ptr(index_cache), code,
-                                    H, D, _ptr(logits), int(logits.stride(0)), _stream(stream)))
+                                    H, D, _ptr(logits), int(logits.stride(0)), int(num_init_tokens),
+                                    int(num_local_tokens), _stream(stream)))
 
 
 def dsa_topk(batch, logits, k, topk_idx, workspace=None, stream=None):

@@ -185,7 +185,8 @@ extern "C" {
 dsa_status_t dsa_indexer_logits(const dsa_batch_t* batch, const void* q, dsa_dtype_t q_dtype,
                                 const float* w, const void* index_cache, dsa_dtype_t k_dtype,
                                 int32_t num_heads, int32_t head_dim, float* logits,
-                                int64_t logits_row_stride, dsa_stream_t stream) {
+                                int64_t logits_row_stride, int32_t num_init_tokens, int32_t num_local_tokens,
+                                dsa_stream_t stream) {
   BatchView bv;
   dsa_status_t st = check_batch(batch, &bv);
   if (st != DSA_OK) return st;
@@ -208,6 +209,9 @@ dsa_status_t dsa_indexer_logits(const dsa_batch_t* batch, const void* q, dsa_dty
                 (long long)logits_row_stride, bv.max_seq_len_k);
   if (bv.num_rows > 0 && (!q || !w || !index_cache || !logits))
     return fail(DSA_ERR_INVALID_ARGUMENT, "q / w / index_cache / logits is NULL");
+  if (num_init_tokens < 0 || num_local_tokens < 0)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "num_init_tokens %d / num_local_tokens %d < 0", num_init_tokens,
+                num_local_tokens);
   if (bv.num_rows == 0 || bv.max_seq_len_k == 0) return ok();
   IndexerParams p;
   p.batch = bv;
@@ -220,9 +224,12 @@ dsa_status_t dsa_indexer_logits(const dsa_batch_t* batch, const void* q, dsa_dty
   p.dim = head_dim;
   p.logits = logits;
   p.stride = logits_row_stride;
+  p.num_init = num_init_tokens;
+  p.num_local = num_local_tokens;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  return from_hip(q_dtype == DSA_FP8_E4M3 ? launch_indexer_fp8(p, s) : launch_indexer_f32(p, s),
-                  "indexer launch");
+  st = from_hip(q_dtype == DSA_FP8_E4M3 ? launch_indexer_fp8(p, s) : launch_indexer_f32(p, s), "indexer launch");
+  if (st != DSA_OK) return st;
+  return from_hip(launch_indexer_force(p, s), "indexer forcing launch");
 }
 
 dsa_status_t dsa_quant_index_q(const void* q, const float* w, int32_t num_rows, int32_t num_heads,

@@ -30,6 +30,8 @@ struct IndexerParams {
   int32_t dim;
   float* logits;
   int64_t stride;
+  int32_t num_init;   // forced positions: the first num_init and the last num_local of a row get +inf
+  int32_t num_local;
 };
 
 struct TopkParams {
@@ -113,6 +115,7 @@ hipError_t launch_quant_index_q(const QuantQParams& p, hipStream_t s);
 hipError_t launch_store_index_k(const StoreKParams& p, hipStream_t s);
 hipError_t launch_indexer_fp8(const IndexerParams& p, hipStream_t s);
 hipError_t launch_indexer_f32(const IndexerParams& p, hipStream_t s);
+hipError_t launch_indexer_force(const IndexerParams& p, hipStream_t s);
 hipError_t launch_topk(const TopkParams& p, hipStream_t s);
 hipError_t launch_mla_bf16(const MlaParams& p, hipStream_t s);
 hipError_t launch_mla_f32(const MlaParams& p, hipStream_t s);

@@ -731,6 +731,31 @@ int resident_wgs() {
 
 }  // namespace
 
+// Init/local-token forcing (SGLang indexer page, Indexer._mask_init_and_local_tokens):
+// +inf at the first num_init and the last num_local visible positions of every
+// row, after the scores are written. One work-group per row.
+__global__ __launch_bounds__(256) void indexer_force_kernel(IndexerParams p) {
+  const BatchView& bv = p.batch;
+  const int t = blockIdx.x;
+  int b, j, q_len;
+  row_to_seq(t, bv.cu_seqlens_q, bv.num_seqs, &b, &j, &q_len);
+  int cap = bv.max_pages_per_seq * bv.page_size;
+  if (cap > bv.max_seq_len_k) cap = bv.max_seq_len_k;
+  if ((int64_t)cap > p.stride) cap = (int)p.stride;
+  const int vis = visible_keys(bv.seq_lens_k[b], q_len, j, cap);
+  const int n_init = min(p.num_init, vis);
+  const int local0 = max(vis - p.num_local, n_init);             // forced tail [local0, vis)
+  float* out = p.logits + (int64_t)t * p.stride;
+  for (int s = threadIdx.x; s < n_init; s += 256) out[s] = INFINITY;
+  for (int s = local0 + threadIdx.x; s < vis; s += 256) out[s] = INFINITY;
+}
+
+hipError_t launch_indexer_force(const IndexerParams& p, hipStream_t s) {
+  if (p.batch.num_rows == 0 || (p.num_init <= 0 && p.num_local <= 0)) return hipSuccess;
+  hipLaunchKernelGGL(indexer_force_kernel, dim3(p.batch.num_rows), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_indexer_fp8(const IndexerParams& p, hipStream_t s) {
   const int chunks = (p.batch.max_seq_len_k + kIdxChunk - 1) / kIdxChunk;
   if (p.batch.num_rows == 0 || chunks == 0) return hipSuccess;

@@ -14,13 +14,14 @@ from . import (DSA_BF16, DSA_F32, DSA_FP8_E4M3, DSA_OP_MLA_DECODE, DSA_OP_MLA_PR
 class DsaStep:
     def __init__(self, *, block_table, seq_lens_k, cu_seqlens_q, page_size, num_pages,
                  max_seq_len_k, max_seq_len_q, num_rows, q_idx, w, index_cache, q_mla, kv_cache,
-                 topk, softmax_scale, d_latent, mla_scales=None):
+                 topk, softmax_scale, d_latent, mla_scales=None, num_init_tokens=0, num_local_tokens=0):
         self.prefill = cu_seqlens_q is not None
         self.batch = make_batch(block_table, seq_lens_k, cu_seqlens_q, page_size=page_size,
                                 num_pages=num_pages, max_seq_len_k=max_seq_len_k,
                                 max_seq_len_q=max_seq_len_q, num_rows=num_rows)
         dev = q_mla.device
         self.q_idx, self.w, self.index_cache = q_idx, w, index_cache
+        self.num_init_tokens, self.num_local_tokens = int(num_init_tokens), int(num_local_tokens)
         self.q_mla, self.kv_cache = q_mla, kv_cache
         self.topk, self.softmax_scale, self.d_latent = int(topk), float(softmax_scale), int(d_latent)
         T, Hm = num_rows, int(q_mla.shape[1])
@@ -43,7 +44,9 @@ class DsaStep:
         self.topk_workspace = torch.empty(tk_bytes, dtype=torch.uint8, device=dev) if tk_bytes else None
 
     def indexer(self, stream=None):
-        dsa_indexer_logits(self.batch, self.q_idx, self.w, self.index_cache, self.logits, stream=stream)
+        dsa_indexer_logits(self.batch, self.q_idx, self.w, self.index_cache, self.logits,
+                           num_init_tokens=self.num_init_tokens, num_local_tokens=self.num_local_tokens,
+                           stream=stream)
 
     def select(self, stream=None):
         dsa_topk(self.batch, self.logits, self.topk, self.topk_idx, self.topk_workspace, stream=stream)

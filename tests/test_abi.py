@@ -103,10 +103,11 @@ def test_empty_batch_is_ok_without_launch(L):
     assert _idx(L, b) == dsa.DSA_OK
 
 
-def _logits(L, batch, qd=dsa.DSA_FP8_E4M3, kd=dsa.DSA_FP8_E4M3, H=64, D=128, stride=256, nullq=False):
+def _logits(L, batch, qd=dsa.DSA_FP8_E4M3, kd=dsa.DSA_FP8_E4M3, H=64, D=128, stride=256, nullq=False,
+            n_init=0, n_local=0):
     return L.dsa_indexer_logits(ctypes.byref(batch), None if nullq else ctypes.c_void_p(0x100), qd,
                                 ctypes.c_void_p(0x200), ctypes.c_void_p(0x300), kd, H, D,
-                                ctypes.c_void_p(0x400), stride, None)
+                                ctypes.c_void_p(0x400), stride, n_init, n_local, None)
 
 
 def test_indexer_validation(L):
@@ -120,6 +121,8 @@ def test_indexer_validation(L):
     assert _logits(L, b, nullq=True) == dsa.DSA_ERR_INVALID_ARGUMENT
     assert _logits(L, b, H=0) == dsa.DSA_ERR_INVALID_ARGUMENT
     assert _logits(L, _batch(num_rows=0, num_seqs=0)) == dsa.DSA_OK
+    assert _logits(L, b, n_init=-1) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert _logits(L, b, n_local=-2) == dsa.DSA_ERR_INVALID_ARGUMENT
 
 
 def _mla(L, batch, decode=True, dtype=dsa.DSA_BF16, H=128, Dl=512, Dr=64, k=2048, ws=None, wsb=0,

@@ -12,6 +12,7 @@ import pytest
 torch = pytest.importorskip("torch")
 
 from dsa_workloads import CONFIGS, generate, small_config  # noqa: E402
+import oracle  # noqa: E402
 from tests import parity  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -138,3 +139,45 @@ def test_empty_batch_launches_nothing():
 
 if __name__ == "__main__":
     sys.exit(pytest.main([__file__, "-v"]))
+
+
+@pytest.mark.parametrize("cfg,n_init,n_local", [
+    (small_config("force_dec", seed=118, lens=[3000, 700, 2100, 5]), 4, 64),
+    (small_config("force_pre", seed=119, lens=[2500, 300], q_lens=[40, 9]), 16, 3),
+    (small_config("force_many", seed=120, lens=[2500], topk=128), 100, 100),
+], ids=["decode", "prefill", "more_than_k"])
+def test_init_and_local_forcing(cfg, n_init, n_local):
+    """The forced positions come out of the indexer as +inf and are always
+    selected; every other logit keeps the parity rule, and top-k is exact on
+    the GPU's logits."""
+    _need_gpu()
+    from dsa_workloads.device import make_step
+    wl = generate(cfg)
+    step = make_step(wl)
+    step.num_init_tokens, step.num_local_tokens = n_init, n_local
+    print(f"\n[parity] {cfg.name}: forcing {n_init} init, {n_local} local", flush=True)
+    step.run()
+    torch.cuda.synchronize()
+    logits = step.logits.cpu().numpy()
+    idx = step.topk_idx.cpu().numpy()
+    vis = parity.visible_of(wl)
+    rows = list(range(wl.num_rows))
+    ref = oracle.indexer_logits(wl.q_idx, wl.w, wl.index_cache, wl.block_table, wl.seq_lens_k,
+                                wl.cu_seqlens_q, cfg.page_size, cfg.idx_kind, rows=rows,
+                                num_init=n_init, num_local=n_local)
+    plain = {t: np.where(np.isinf(ref[t]) & (ref[t] > 0), 0.0, ref[t]) for t in rows}
+    for t in rows:
+        n = vis[t]
+        forced = np.isposinf(ref[t])
+        assert np.array_equal(np.isposinf(logits[t][:n]), forced), f"row {t}: forced positions differ"
+        got = logits[t][:n].copy()
+        got[forced] = 0.0
+        parity.check_logits({t: got}, wl, [t], ref={t: plain[t]})
+    parity.check_topk_exact(idx, logits, vis, cfg.topk, rows)
+    for t in rows:
+        forced = set(np.nonzero(np.isposinf(ref[t]))[0].tolist())
+        chosen = set(int(x) for x in idx[t] if x >= 0)
+        if len(forced) <= cfg.topk:
+            assert forced <= chosen, f"row {t}: a forced position was not selected"
+        else:
+            assert chosen == set(sorted(forced)[:cfg.topk])
