@@ -11,6 +11,7 @@ import pytest
 torch = pytest.importorskip("torch")
 
 from dsa_workloads import generate, small_config  # noqa: E402
+from tests import parity  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -25,17 +26,24 @@ def _snapshot(step):
     }
 
 
-@pytest.mark.parametrize("lens", [[3000, 700, 5000, 64], [9000]])
-def test_graph_replays_match_eager(lens):
+@pytest.mark.parametrize("lens,q_lens,mla_kind,forcing", [
+    ([3000, 700, 5000, 64], (), "bf16", (0, 0)),
+    ([9000], (), "bf16", (0, 0)),
+    ([3000, 700, 5000], (), "fp8", (4, 32)),                 # fp8 latent cache, init/local forcing
+    ([2500, 2100], (2, 2), "bf16", (0, 0)),                  # multi-token decode
+], ids=["decode", "long_row", "fp8_forced", "mtp"])
+def test_graph_replays_match_eager(lens, q_lens, mla_kind, forcing):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     from dsa_workloads.device import make_step
-    cfg = small_config(f"graph_{len(lens)}", seed=211, lens=lens)
-    print(f"\n[graph] {cfg.name}: lens {lens}", flush=True)
-    step = make_step(generate(cfg))
+    cfg = small_config(f"graph_{len(lens)}_{mla_kind}", seed=211, lens=lens, q_lens=q_lens, mla_kind=mla_kind)
+    print(f"\n[graph] {cfg.name}: lens {lens} q_lens {q_lens} forcing {forcing}", flush=True)
+    wl = generate(cfg)
+    step = make_step(wl)
+    step.num_init_tokens, step.num_local_tokens = forcing
     step.run()
     want = _snapshot(step)
-    vis = [min(int(n), want["logits"].shape[1]) for n in lens]
+    vis = parity.visible_of(wl)                         # per query row (multi-token rows see fewer keys)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
