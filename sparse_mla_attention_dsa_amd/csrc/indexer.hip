@@ -149,21 +149,23 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_fp8_kernel(IndexerPara
 // request (multi-token decode, where a request carries next_n <= 4 rows and
 // row i sees one key more than row i - 1; the SGLang indexer page scores the
 // next_n rows of a request against the same paged keys). The keys of every
-// unit are cut into groups of 16 (ceil(visible / 16) for its last row); every
-// wave of a fixed grid takes an equal contiguous share of the flattened group
-// list, whatever the lengths, and walks it in batches of up to four groups
-// inside one page. The batch list of a wave is built once (lane j holds batch
-// j's unit, first group, count, page and row lengths; all page lookups in one
-// vector load), then the wave streams: the loads of batch j + 1 are issued
-// before the MFMAs of batch j, and each key group meets the q of every row of
-// its unit. q and the head weights are reloaded when the unit changes (once or
-// twice per wave). Every wave is independent: no barrier after the unit
-// prefix sums.
-constexpr int kStreamThreads = 256;
-constexpr int kStreamWaves = kStreamThreads / kWave;
+// unit are cut into groups of 16 (ceil(visible / 16) for its last row), and
+// the groups into chunks: up to four groups inside one page. Every work-group
+// (one per CU) takes an equal contiguous share of the flattened chunk list,
+// whatever the lengths, writes a record per chunk into LDS (unit, first group,
+// count, page, rows and their lengths; all page lookups at once), and its
+// waves then take chunks one at a time from an LDS counter, so that the waves
+// a CU issues first (which run ahead) take more of them and the CU's waves
+// finish together. A wave issues the loads of its next chunk before the MFMAs
+// of the current one, and each key group meets the q of every row of its
+// unit; q and the head weights are reloaded when the unit changes.
 constexpr int kStreamMaxUnits = 1024;
-constexpr int kStreamBatch = 4;                                  // groups per batch
+constexpr int kStreamBatch = 4;                                  // groups per chunk
 constexpr int kStreamMaxQLen = 4;                                // rows per request, multi-row units
+constexpr int kStreamMaxChunks = 1024;                           // chunk records per round
+
+// Waves per work-group: as many as the registers let one CU hold
+template <int kR> constexpr int stream_waves() { return kR == 1 ? 12 : 8; }
 
 // Unit u of a stream launch with kR rows per unit. kR = 1: unit u is decode
 // row u. kR = 2: unit u is rows 2 (u & 1) and 2 (u & 1) + 1 of request u >> 1
@@ -192,10 +194,20 @@ __device__ __forceinline__ void stream_unit(const BatchView& bv, int u, int cap,
   *vis_last = n > 0 ? visible_keys(len, q_len, 2 * half + n - 1, cap) : 0;
 }
 
-template <int kR, int kAhead>
-__global__ __launch_bounds__(kStreamThreads) void indexer_fp8_stream_kernel(IndexerParams p) {
-  __shared__ int pre[kStreamMaxUnits + 1];                       // group prefix over units
-  __shared__ int wsum[kStreamWaves];
+// chunks of a unit with n groups, gpp groups per page and cpp chunks per full page
+__device__ __forceinline__ int stream_chunks(int n, int gpp, int cpp) {
+  return (n / gpp) * cpp + (n % gpp + kStreamBatch - 1) / kStreamBatch;
+}
+
+template <int kR>
+__global__ __launch_bounds__(stream_waves<kR>() * kWave) void indexer_fp8_stream_kernel(IndexerParams p) {
+  constexpr int kWaves = stream_waves<kR>();
+  constexpr int kThreads = kWaves * kWave;
+  __shared__ int pre[kStreamMaxUnits + 1];                       // chunk prefix over units
+  __shared__ int wsum[kWaves];
+  __shared__ int4 rec_a[kStreamMaxChunks];                       // unit, first group, groups, page
+  __shared__ int4 rec_b[kStreamMaxChunks];                       // first row, rows, visible keys of first / last row
+  __shared__ int next_chunk;
   const BatchView& bv = p.batch;
   const int U = kR == 1 ? bv.num_rows : 2 * bv.num_seqs;         // units
   const int tid = threadIdx.x;
@@ -204,26 +216,27 @@ __global__ __launch_bounds__(kStreamThreads) void indexer_fp8_stream_kernel(Inde
   const int g = lane >> 4, c = lane & 15;
   const int P = bv.page_size;
   const int gpp = P / 16;                                        // groups per page
+  const int cpp = (gpp + kStreamBatch - 1) / kStreamBatch;       // chunks per full page
   int cap = bv.max_pages_per_seq * P;
   if (cap > bv.max_seq_len_k) cap = bv.max_seq_len_k;
   if ((int64_t)cap > p.stride) cap = (int)p.stride;
 
-  // ---- groups per unit and their prefix sums ----
+  // ---- chunks per unit and their prefix sums ----
   int carry = 0;
-  for (int base = 0; base < U; base += kStreamThreads) {
+  for (int base = 0; base < U; base += kThreads) {
     const int u = base + tid;
     int cnt = 0;
     if (u < U) {
       int b_, r0_, nr_, vf_, vl_;
       stream_unit<kR>(bv, u, cap, &b_, &r0_, &nr_, &vf_, &vl_);
-      cnt = (vl_ + 15) >> 4;
+      cnt = stream_chunks((vl_ + 15) >> 4, gpp, cpp);
     }
     const int incl = (int)wave_inclusive_scan((uint32_t)cnt);
     if (lane == kWave - 1) wsum[wave] = incl;
     __syncthreads();
     int before = 0, tot = 0;
 #pragma unroll
-    for (int w = 0; w < kStreamWaves; ++w) {
+    for (int w = 0; w < kWaves; ++w) {
       const int v = wsum[w];
       before += (w < wave) ? v : 0;
       tot += v;
@@ -235,127 +248,118 @@ __global__ __launch_bounds__(kStreamThreads) void indexer_fp8_stream_kernel(Inde
   if (tid == 0) pre[0] = 0;
   __syncthreads();
 
-  const int N = pre[U];
-  const int W = gridDim.x * kStreamWaves;
-  const int wg = blockIdx.x * kStreamWaves + wave;
-  int a = (int)((int64_t)N * wg / W);
-  const int a_end = (int)((int64_t)N * (wg + 1) / W);
-  if (a >= a_end) return;
-  // unit of group a: the largest t with pre[t] <= a (units without groups are passed over)
-  int t = 0;
-  {
-    int lo = 0, hi = U - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (pre[mid] <= a) lo = mid; else hi = mid - 1;
-    }
-    t = lo;
-  }
-  t = __builtin_amdgcn_readfirstlane(t);
-  int gi = a - pre[t];
-  gi = __builtin_amdgcn_readfirstlane(gi);
+  const int C = pre[U];
+  const int c_begin = (int)((int64_t)C * blockIdx.x / gridDim.x);
+  const int c_end = (int)((int64_t)C * (blockIdx.x + 1) / gridDim.x);
 
   const int64_t scale_off = (int64_t)P * kIdxDim;
   const uint8_t* cache = p.cache;
-  while (a < a_end) {
-    // ---- batch list (up to 64 batches): lane j holds batch j ----
-    int bt_t = 0, bt_gi = 0, bt_cnt = 0, nb = 0;
-    while (a < a_end && nb < kWave) {
-      int n_t = pre[t + 1] - pre[t];
-      while (gi >= n_t) {                                        // next unit with groups
-        ++t;
-        gi = 0;
-        n_t = pre[t + 1] - pre[t];
-      }
-      int gend = (gi / gpp + 1) * gpp;
-      gend = min(gend, gi + kStreamBatch);
-      gend = min(gend, n_t);
-      gend = min(gend, gi + (a_end - a));
-      if (lane == nb) { bt_t = t; bt_gi = gi; bt_cnt = gend - gi; }
-      a += gend - gi;
-      gi = gend;
-      ++nb;
-    }
-    // pages, first rows and row lengths of every batch in one go
-    int bt_page = -1, bt_r0 = 0, bt_nr = 0, bt_vf = 0, bt_vl = 0;
-    if (lane < nb) {
-      int b_;
-      stream_unit<kR>(bv, bt_t, cap, &b_, &bt_r0, &bt_nr, &bt_vf, &bt_vl);
-      bt_page = bv.block_table[(int64_t)b_ * bv.max_pages_per_seq + bt_gi / gpp];
-    }
 
-    struct Batch { int t, gi, cnt, page, r0, nr, vf, vl; };
-    auto batch_of = [&](int j) {
-      Batch x;
-      x.t = __builtin_amdgcn_readlane(bt_t, j);
-      x.gi = __builtin_amdgcn_readlane(bt_gi, j);
-      x.cnt = __builtin_amdgcn_readlane(bt_cnt, j);
-      x.page = __builtin_amdgcn_readlane(bt_page, j);
-      x.r0 = __builtin_amdgcn_readlane(bt_r0, j);
-      x.nr = kR == 1 ? 1 : __builtin_amdgcn_readlane(bt_nr, j);
-      x.vf = __builtin_amdgcn_readlane(bt_vf, j);
-      x.vl = kR == 1 ? x.vf : __builtin_amdgcn_readlane(bt_vl, j);
-      return x;
-    };
-    // key operands (lane (c, g): key 16u + c of the batch, bytes [32g, 32g + 32)) and scales
-    auto load_batch = [&](const Batch& x, i32x8 (&kb)[kStreamBatch], float (&sg)[kStreamBatch]) {
-      const bool okp = x.page >= 0 && x.page < bv.num_pages;
-      const uint8_t* pg = cache + (int64_t)(okp ? x.page : 0) * p.page_bytes;
+  struct Batch { int t, gi, cnt, page, r0, nr, vf, vl; };
+  auto record = [&](int j) {                                     // chunk j of the round, wave-uniform
+    const int4 a = rec_a[j];
+    const int4 b = rec_b[j];
+    Batch x;
+    x.t = __builtin_amdgcn_readfirstlane(a.x);
+    x.gi = __builtin_amdgcn_readfirstlane(a.y);
+    x.cnt = __builtin_amdgcn_readfirstlane(a.z);
+    x.page = __builtin_amdgcn_readfirstlane(a.w);
+    x.r0 = __builtin_amdgcn_readfirstlane(b.x);
+    x.nr = kR == 1 ? 1 : __builtin_amdgcn_readfirstlane(b.y);
+    x.vf = __builtin_amdgcn_readfirstlane(b.z);
+    x.vl = kR == 1 ? x.vf : __builtin_amdgcn_readfirstlane(b.w);
+    return x;
+  };
+  auto take = [&]() {                                            // next chunk of the round, wave-uniform
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&next_chunk, 1);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  // key operands (lane (c, g): key 16u + c of the chunk, bytes [32g, 32g + 32)) and scales
+  auto load_batch = [&](const Batch& x, i32x8 (&kb)[kStreamBatch], float (&sg)[kStreamBatch]) {
+    const bool okp = x.page >= 0 && x.page < bv.num_pages;
+    const uint8_t* pg = cache + (int64_t)(okp ? x.page : 0) * p.page_bytes;
 #pragma unroll
-      for (int u = 0; u < kStreamBatch; ++u) {
-        const int uu = u < x.cnt ? u : 0;                        // past the batch: re-read group 0
-        const int slot = (16 * (x.gi + uu)) % P + c;
-        kb[u] = *reinterpret_cast<const i32x8*>(pg + (int64_t)slot * kIdxDim + 32 * g);
-        sg[u] = *reinterpret_cast<const float*>(pg + scale_off + 4 * slot);
-      }
-    };
+    for (int u = 0; u < kStreamBatch; ++u) {
+      const int uu = u < x.cnt ? u : 0;                          // past the chunk: re-read group 0
+      const int slot = (16 * (x.gi + uu)) % P + c;
+      kb[u] = *reinterpret_cast<const i32x8*>(pg + (int64_t)slot * kIdxDim + 32 * g);
+      sg[u] = *reinterpret_cast<const float*>(pg + scale_off + 4 * slot);
+    }
+  };
 
-    // q of the unit's rows as 16-head A operands (lane (c, g): head 16m + c,
-    // bytes [32g, 32g + 32)) and their head weights in accumulator order
-    i32x8 qa[kR][4];
-    float wv[kR][16];
-    int q_unit = -1;
-    auto load_unit = [&](const Batch& x) {
+  // q of the unit's rows as 16-head A operands (lane (c, g): head 16m + c,
+  // bytes [32g, 32g + 32)) and their head weights in accumulator order
+  i32x8 qa[kR][4];
+  float wv[kR][16];
+  int q_unit = -1;
+  auto load_unit = [&](const Batch& x) {
 #pragma unroll
-      for (int r = 0; r < kR; ++r) {
-        if (r < x.nr) {
-          const int row = x.r0 + r;
-          const uint8_t* qr = static_cast<const uint8_t*>(p.q) + (int64_t)row * (kIdxHeads * kIdxDim);
+    for (int r = 0; r < kR; ++r) {
+      if (r < x.nr) {
+        const int row = x.r0 + r;
+        const uint8_t* qr = static_cast<const uint8_t*>(p.q) + (int64_t)row * (kIdxHeads * kIdxDim);
 #pragma unroll
-          for (int m = 0; m < 4; ++m)
-            qa[r][m] = *reinterpret_cast<const i32x8*>(qr + (16 * m + c) * kIdxDim + 32 * g);
-          const float* wrow = p.w + (int64_t)row * kIdxHeads;
+        for (int m = 0; m < 4; ++m)
+          qa[r][m] = *reinterpret_cast<const i32x8*>(qr + (16 * m + c) * kIdxDim + 32 * g);
+        const float* wrow = p.w + (int64_t)row * kIdxHeads;
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const f32x4 w4 = *reinterpret_cast<const f32x4*>(wrow + 16 * m + 4 * g);
+        for (int m = 0; m < 4; ++m) {
+          const f32x4 w4 = *reinterpret_cast<const f32x4*>(wrow + 16 * m + 4 * g);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) wv[r][4 * m + i] = w4[i];
-          }
+          for (int i = 0; i < 4; ++i) wv[r][4 * m + i] = w4[i];
         }
       }
-      q_unit = x.t;
-    };
-
-    // kAhead batches in flight ahead of the one being computed
-    Batch bq[kAhead + 1];
-    i32x8 kb[kAhead + 1][kStreamBatch];
-    float sg[kAhead + 1][kStreamBatch];
-#pragma unroll
-    for (int d = 0; d < kAhead; ++d) {
-      if (d < nb) {
-        bq[d] = batch_of(d);
-        load_batch(bq[d], kb[d], sg[d]);
-      }
     }
-    load_unit(bq[0]);
-    for (int j = 0; j < nb; ++j) {
-      if (j + kAhead < nb) {
-        bq[kAhead] = batch_of(j + kAhead);
-        load_batch(bq[kAhead], kb[kAhead], sg[kAhead]);
+    q_unit = x.t;
+  };
+
+  for (int round = c_begin; round < c_end; round += kStreamMaxChunks) {
+    const int n = min(kStreamMaxChunks, c_end - round);
+    // ---- the round's chunk records ----
+    for (int i = tid; i < n; i += kThreads) {
+      const int ch = round + i;
+      int lo = 0, hi = U - 1;                                    // unit: the largest t with pre[t] <= ch
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= ch) lo = mid; else hi = mid - 1;
       }
-      const Batch& cur = bq[0];
+      int b_, r0_, nr_, vf_, vl_;
+      stream_unit<kR>(bv, lo, cap, &b_, &r0_, &nr_, &vf_, &vl_);
+      const int n_t = (vl_ + 15) >> 4;
+      const int cu = ch - pre[lo];
+      const int pgi = cu / cpp;                                  // page index inside the unit
+      const int gi = pgi * gpp + kStreamBatch * (cu - pgi * cpp);
+      const int gend = min(min(gi + kStreamBatch, (pgi + 1) * gpp), n_t);
+      const int page = bv.block_table[(int64_t)b_ * bv.max_pages_per_seq + pgi];
+      rec_a[i] = make_int4(lo, gi, gend - gi, page);
+      rec_b[i] = make_int4(r0_, nr_, vf_, vl_);
+    }
+    if (tid == 0) next_chunk = 0;
+    __syncthreads();
+
+    // ---- the waves take chunks until the round is done: a wave holds the
+    // chunk it computes (its keys loaded) and the next one (loads issued
+    // before the MFMAs), and takes the one after during the MFMAs ----
+    i32x8 kb[2][kStreamBatch];
+    float sg[2][kStreamBatch];
+    int j = take();
+    Batch cur = {};
+    if (j < n) {
+      cur = record(j);
+      load_batch(cur, kb[0], sg[0]);
+    }
+    int jn = j < n ? take() : n;
+    while (j < n) {
+      Batch nx = {};
+      if (jn < n) {
+        nx = record(jn);
+        load_batch(nx, kb[1], sg[1]);
+      }
+      int jnn = n;                                               // read after the MFMAs
+      if (lane == 0 && jn < n) jnn = atomicAdd(&next_chunk, 1);
       if (cur.t != q_unit) load_unit(cur);
-      // ---- logits of batch j, for every row of its unit ----
+      // ---- logits of the chunk, for every row of its unit ----
       const bool okp = cur.page >= 0 && cur.page < bv.num_pages;
 #pragma unroll
       for (int r = 0; r < kR; ++r) {
@@ -380,14 +384,13 @@ __global__ __launch_bounds__(kStreamThreads) void indexer_fp8_stream_kernel(Inde
           if (g == 0 && s < vis) out[s] = okp ? part * sg[0][u] : -INFINITY;
         }
       }
-      if (j + 1 >= nb) break;
+      cur = nx;
 #pragma unroll
-      for (int d = 0; d < kAhead; ++d) {
-        bq[d] = bq[d + 1];
-#pragma unroll
-        for (int u = 0; u < kStreamBatch; ++u) { kb[d][u] = kb[d + 1][u]; sg[d][u] = sg[d + 1][u]; }
-      }
+      for (int u = 0; u < kStreamBatch; ++u) { kb[0][u] = kb[1][u]; sg[0][u] = sg[1][u]; }
+      j = jn;
+      jn = jn < n ? __builtin_amdgcn_readfirstlane(jnn) : n;
     }
+    __syncthreads();                                             // records free for the next round
   }
 }
 
@@ -704,9 +707,9 @@ __global__ __launch_bounds__(kF32Block) void indexer_f32_kernel(IndexerParams p)
 }
 
 // Work-groups of a stream kernel that the current device holds at once: CUs
-// times the occupancy the kernel's registers and LDS allow. Queried once per
-// device and kernel (host calls only, nothing is enqueued).
-template <int kR, int kAhead>
+// times the occupancy the kernel's registers and LDS allow (one per CU).
+// Queried once per device and kernel (host calls only, nothing is enqueued).
+template <int kR>
 int resident_wgs() {
   constexpr int kMaxDevices = 64;
   static std::atomic<int> cache[kMaxDevices];
@@ -718,11 +721,11 @@ int resident_wgs() {
   }
   int cus = 0, per_cu = 0;
   if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, indexer_fp8_stream_kernel<kR, kAhead>,
-                                                   kStreamThreads, 0) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, indexer_fp8_stream_kernel<kR>,
+                                                   stream_waves<kR>() * kWave, 0) != hipSuccess ||
       cus < 1 || per_cu < 1) {
     (void)hipGetLastError();
-    return 256 * (kR == 1 ? 3 : 2);                              // MI355X: 256 CUs
+    return 256;                                                  // MI355X: 256 CUs
   }
   const int v = cus * per_cu;
   if (dev >= 0) cache[dev].store(v, std::memory_order_relaxed);
@@ -763,20 +766,22 @@ hipError_t launch_indexer_fp8(const IndexerParams& p, hipStream_t s) {
   const bool multi = p.batch.cu_seqlens_q != nullptr && p.batch.max_seq_len_q <= kStreamMaxQLen &&
                      2 * p.batch.num_seqs <= kStreamMaxUnits;
   if (decode || multi) {
-    // about 32 groups per wave, and no more work-groups than are resident at
+    // spread over as many CUs as there are chunks for one per wave (a bound
+    // from the longest row), and no more work-groups than are resident at
     // once (one round: a second round would start late and finish last)
     const int64_t units = decode ? p.batch.num_rows : std::min<int64_t>(p.batch.num_rows, 2LL * p.batch.num_seqs);
-    const int64_t groups = units * ((p.batch.max_seq_len_k + 15) / 16);
-    int64_t wgs = (groups / 32 + kStreamWaves - 1) / kStreamWaves;
-    const int resident = decode ? resident_wgs<1, 1>() : resident_wgs<2, 1>();
+    const int64_t chunks = units * ((p.batch.max_seq_len_k + 16 * kStreamBatch - 1) / (16 * kStreamBatch));
+    const int waves = decode ? stream_waves<1>() : stream_waves<2>();
+    int64_t wgs = (chunks + waves - 1) / waves;
+    const int resident = decode ? resident_wgs<1>() : resident_wgs<2>();
     if (wgs > resident) wgs = resident;
     if (wgs < 1) wgs = 1;
     if (decode)
-      hipLaunchKernelGGL(HIP_KERNEL_NAME(indexer_fp8_stream_kernel<1, 1>), dim3((unsigned)wgs),
-                         dim3(kStreamThreads), 0, s, p);
+      hipLaunchKernelGGL(HIP_KERNEL_NAME(indexer_fp8_stream_kernel<1>), dim3((unsigned)wgs),
+                         dim3(stream_waves<1>() * kWave), 0, s, p);
     else
-      hipLaunchKernelGGL(HIP_KERNEL_NAME(indexer_fp8_stream_kernel<2, 1>), dim3((unsigned)wgs),
-                         dim3(kStreamThreads), 0, s, p);
+      hipLaunchKernelGGL(HIP_KERNEL_NAME(indexer_fp8_stream_kernel<2>), dim3((unsigned)wgs),
+                         dim3(stream_waves<2>() * kWave), 0, s, p);
     return hipGetLastError();
   }
   if (p.batch.cu_seqlens_q != nullptr && p.batch.num_seqs <= kPfMaxSeqs && p.stride <= kPfMaxStride) {
