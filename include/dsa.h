@@ -126,6 +126,8 @@ typedef struct {
  *           and s >= visible(t) - num_local_tokens of each row (s < visible(t))
  *           get +inf, so that dsa_topk always selects them (ties at +inf go to
  *           the lower positions). 0 and 0 turn it off.
+ * With FP8_E4M3, q, w and index_cache must be 16-byte aligned
+ * (DSA_ERR_INVALID_ARGUMENT otherwise).
  */
 dsa_status_t dsa_indexer_logits(const dsa_batch_t *batch,
                                 const void *q, dsa_dtype_t q_dtype,
@@ -228,6 +230,8 @@ dsa_status_t dsa_topk(const dsa_batch_t *batch,
  * out:      [T, Hm, d_latent] in dtype.   lse: [T, Hm] fp32, may be NULL.
  * workspace: at least dsa_workspace_bytes(DSA_OP_MLA_DECODE or _PREFILL, ...)
  *           bytes of device memory (split-KV partial results); NULL if that is 0.
+ * With BF16, q, kv_cache, out and a non-empty workspace must be 16-byte
+ * aligned (DSA_ERR_INVALID_ARGUMENT otherwise).
  *
  * sparse_mla_decode requires cu_seqlens_q == NULL (one row per request);
  * sparse_mla_prefill requires cu_seqlens_q != NULL.
@@ -270,6 +274,8 @@ dsa_status_t sparse_mla_prefill(const dsa_batch_t *batch,
  * workspace: at least dsa_workspace_bytes(DSA_OP_MLA_DECODE or _PREFILL, ...,
  *           DSA_FP8_E4M3) bytes (split partials; always at least two splits
  *           when k > 1024); NULL if that is 0.
+ * q, kv_cache, out and the workspace must be 16-byte aligned
+ * (DSA_ERR_INVALID_ARGUMENT otherwise).
  */
 dsa_status_t sparse_mla_decode_fp8(const dsa_batch_t *batch,
                                    const void *q, float q_scale,

@@ -34,6 +34,8 @@ dsa_status_t from_hip(hipError_t e, const char* what) {
 }
 
 // Checks shared by every entry point; fills `bv` on success.
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
 dsa_status_t check_batch(const dsa_batch_t* batch, BatchView* bv) {
   if (!batch) return fail(DSA_ERR_INVALID_ARGUMENT, "batch is NULL");
   const dsa_batch_t& b = *batch;
@@ -148,6 +150,9 @@ dsa_status_t run_mla(const dsa_batch_t* batch, bool decode, const void* q, const
     return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, plan.workspace);
   if (plan.workspace > 0 && !workspace)
     return fail(DSA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if ((plan.bf16 || plan.fp8) && bv.num_rows > 0 &&
+      !(aligned16(q) && aligned16(kv_cache) && aligned16(out) && (plan.workspace == 0 || aligned16(workspace))))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "q, kv_cache, out and workspace must be 16-byte aligned");
   if (bv.num_rows == 0) return ok();
 
   MlaParams p;
@@ -212,6 +217,8 @@ dsa_status_t dsa_indexer_logits(const dsa_batch_t* batch, const void* q, dsa_dty
   if (num_init_tokens < 0 || num_local_tokens < 0)
     return fail(DSA_ERR_INVALID_ARGUMENT, "num_init_tokens %d / num_local_tokens %d < 0", num_init_tokens,
                 num_local_tokens);
+  if (q_dtype == DSA_FP8_E4M3 && bv.num_rows > 0 && !(aligned16(q) && aligned16(w) && aligned16(index_cache)))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "q, w and index_cache must be 16-byte aligned");
   if (bv.num_rows == 0 || bv.max_seq_len_k == 0) return ok();
   IndexerParams p;
   p.batch = bv;

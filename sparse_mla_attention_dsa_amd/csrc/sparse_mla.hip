@@ -508,36 +508,49 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
 }
 
 // LSE merge of the split partials (merge_attn_states generalised to S parts).
-// 256 threads cover two heads of one row; each thread owns four value columns.
-template <bool kBf16Out>
+// 256 threads cover four heads of one row; each thread owns eight value
+// columns, so every partial arrives in one 16-byte load. With the split count
+// known at compile time (kS > 0) all loads of a thread are issued together.
+template <int kS>
 __global__ __launch_bounds__(256) void mla_combine_kernel(MlaParams p) {
   const int t = blockIdx.x;
-  const int h = 2 * blockIdx.y + (threadIdx.x >> 7);
-  const int d4 = threadIdx.x & 127;                 // value columns 4*d4 .. 4*d4+3
-  const int S = p.splits, Hm = p.heads, Dl = p.d_latent;
-  if (h >= Hm || 4 * d4 >= Dl) return;
+  const int h = 4 * blockIdx.y + (threadIdx.x >> 6);
+  const int d8 = threadIdx.x & 63;                  // value columns 8*d8 .. 8*d8+7
+  const int S = kS > 0 ? kS : p.splits, Hm = p.heads;
+  if (h >= Hm) return;
   const float* pl = p.part_lse + (int64_t)t * S * Hm + h;
-  float mx = -INFINITY;
-  for (int s = 0; s < S; ++s) mx = fmaxf(mx, pl[(int64_t)s * Hm]);
-  float tot = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < S; ++s) {
-    const float l = pl[(int64_t)s * Hm];
+  const uint16_t* po = p.part_o + ((int64_t)t * S * Hm + h) * kMlaDl + 8 * d8;
+  const int64_t o_stride = (int64_t)Hm * kMlaDl;    // next split's partial of the same head
+  float mx = -INFINITY, tot = 0.f;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+  auto add = [&](float l, const bf16x8& ob) {       // wgt = exp(l - mx), mx final
     const float wgt = (l == -INFINITY) ? 0.f : __expf(l - mx);
     tot += wgt;
-    const bf16x4 ob = *reinterpret_cast<const bf16x4*>(p.part_o + (((int64_t)t * S + s) * Hm + h) * Dl + 4 * d4);
-    const f32x4 o = __builtin_convertvector(ob, f32x4);
-    acc += wgt * o;
+    acc0 += wgt * __builtin_convertvector(__builtin_shufflevector(ob, ob, 0, 1, 2, 3), f32x4);
+    acc1 += wgt * __builtin_convertvector(__builtin_shufflevector(ob, ob, 4, 5, 6, 7), f32x4);
+  };
+  if (kS > 0) {
+    float l[kS > 0 ? kS : 1];
+    bf16x8 ob[kS > 0 ? kS : 1];
+#pragma unroll
+    for (int s = 0; s < kS; ++s) {
+      l[s] = pl[(int64_t)s * Hm];
+      ob[s] = *reinterpret_cast<const bf16x8*>(po + s * o_stride);
+    }
+#pragma unroll
+    for (int s = 0; s < kS; ++s) mx = fmaxf(mx, l[s]);
+#pragma unroll
+    for (int s = 0; s < kS; ++s) add(l[s], ob[s]);
+  } else {
+    for (int s = 0; s < S; ++s) mx = fmaxf(mx, pl[(int64_t)s * Hm]);
+    for (int s = 0; s < S; ++s) add(pl[(int64_t)s * Hm], *reinterpret_cast<const bf16x8*>(po + s * o_stride));
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
-  acc *= inv;
-  if (d4 == 0 && p.lse) p.lse[(int64_t)t * Hm + h] = tot > 0.f ? mx + __logf(tot) : -INFINITY;
-  if (kBf16Out) {
-    const bf16x4 o = __builtin_convertvector(acc, bf16x4);
-    *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(p.out) + ((int64_t)t * Hm + h) * Dl + 4 * d4) = o;
-  } else {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + ((int64_t)t * Hm + h) * Dl + 4 * d4) = acc;
-  }
+  if (d8 == 0 && p.lse) p.lse[(int64_t)t * Hm + h] = tot > 0.f ? mx + __logf(tot) : -INFINITY;
+  const bf16x4 lo = __builtin_convertvector(acc0 * inv, bf16x4);
+  const bf16x4 hi = __builtin_convertvector(acc1 * inv, bf16x4);
+  *reinterpret_cast<bf16x8*>(static_cast<uint16_t*>(p.out) + ((int64_t)t * Hm + h) * kMlaDl + 8 * d8) =
+      __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // fp32 path for small shapes: one work-group per (row, head), two-pass softmax.
@@ -652,7 +665,13 @@ hipError_t launch_mla_bf16(const MlaParams& p, hipStream_t s) {
 }
 
 hipError_t launch_mla_combine_bf16(const MlaParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(mla_combine_kernel<true>, dim3(p.batch.num_rows, (p.heads + 1) / 2), dim3(256), 0, s, p);
+  const dim3 grid(p.batch.num_rows, (p.heads + 3) / 4);
+  if (p.splits == 2)
+    hipLaunchKernelGGL(mla_combine_kernel<2>, grid, dim3(256), 0, s, p);
+  else if (p.splits == 4)
+    hipLaunchKernelGGL(mla_combine_kernel<4>, grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(mla_combine_kernel<0>, grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -125,6 +125,16 @@ def test_indexer_validation(L):
     assert _logits(L, b, n_local=-2) == dsa.DSA_ERR_INVALID_ARGUMENT
 
 
+@pytest.mark.parametrize("which", ["q", "w", "cache"])
+def test_fp8_indexer_rejects_misaligned_pointers(L, which):
+    ptr = {"q": 0x100, "w": 0x200, "cache": 0x300}
+    ptr[which] += 4
+    V = ctypes.c_void_p
+    st = L.dsa_indexer_logits(ctypes.byref(_batch()), V(ptr["q"]), dsa.DSA_FP8_E4M3, V(ptr["w"]), V(ptr["cache"]),
+                              dsa.DSA_FP8_E4M3, 64, 128, V(0x400), 256, 0, 0, None)
+    assert st == dsa.DSA_ERR_INVALID_ARGUMENT
+
+
 def _mla(L, batch, decode=True, dtype=dsa.DSA_BF16, H=128, Dl=512, Dr=64, k=2048, ws=None, wsb=0,
          scale=0.07, nullout=False):
     fn = L.sparse_mla_decode if decode else L.sparse_mla_prefill
@@ -155,6 +165,24 @@ def test_mla_validation(L):
     assert L.dsa_workspace_bytes(dsa.DSA_OP_MLA_PREFILL, ctypes.byref(pre), 2048, 128, 512, dsa.DSA_BF16) == 0
     assert _mla(L, dsa.DsaBatch(**{**{f: getattr(pre, f) for f, _ in dsa.DsaBatch._fields_},
                                    "num_rows": 0, "num_seqs": 1}), decode=False) == dsa.DSA_OK
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("which", ["q", "kv", "out", "ws"])
+def test_attention_rejects_misaligned_pointers(L, fp8, which):
+    dec = _batch(num_seqs=64, num_rows=64)
+    dt = dsa.DSA_FP8_E4M3 if fp8 else dsa.DSA_BF16
+    need = L.dsa_workspace_bytes(dsa.DSA_OP_MLA_DECODE, ctypes.byref(dec), 2048, 128, 512, dt)
+    ptr = {"q": 0x10, "kv": 0x20, "out": 0x40, "ws": 0x1000}
+    ptr[which] += 8
+    V = ctypes.c_void_p
+    if fp8:
+        st = L.sparse_mla_decode_fp8(ctypes.byref(dec), V(ptr["q"]), 0.02, V(ptr["kv"]), 0.01, V(0x30), 2048,
+                                     128, 512, 64, 0.07, V(ptr["out"]), None, V(ptr["ws"]), need, None)
+    else:
+        st = L.sparse_mla_decode(ctypes.byref(dec), V(ptr["q"]), V(ptr["kv"]), dt, V(0x30), 2048, 128, 512, 64,
+                                 0.07, V(ptr["out"]), None, V(ptr["ws"]), need, None)
+    assert st == dsa.DSA_ERR_INVALID_ARGUMENT
 
 
 def test_topk_workspace_for_few_long_rows(L):
