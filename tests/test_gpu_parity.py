@@ -124,6 +124,41 @@ def test_full_prefill_sampled():
     _full_check(CONFIGS["prefill_4k_on_16k"], rows=[0, 1, 2047, 4094, 4095])
 
 
+def test_indexer_chunk_records_in_rounds():
+    """1,024 decode rows of 15-20k keys over a shared pool of 320 pages (rows
+    may name the same page, as shared prefixes do): every work-group of the
+    stream indexer owns more chunks than its LDS record table holds (1,024)
+    and takes them in two rounds. Sampled rows against the oracle."""
+    _need_gpu()
+    import types
+    import sparse_mla_attention_dsa_amd as dsa
+    from dsa_workloads import _to_e4m3fn_bytes
+    rng = np.random.default_rng(620)
+    B, P, pool, H, D = 1024, 64, 320, 64, 128
+    lens = rng.integers(15000, 20001, size=B).astype(np.int32)
+    max_len = int(lens.max())
+    bt = rng.integers(0, pool, size=(B, -(-max_len // P))).astype(np.int32)
+    keys = rng.standard_normal((pool * P, D)).astype(np.float32)
+    sig = (np.abs(keys).max(axis=1) / 448.0).astype(np.float32)
+    codes = _to_e4m3fn_bytes(keys / sig[:, None])
+    cache = np.concatenate([codes.reshape(pool, P * D), sig.reshape(pool, P).view(np.uint8).reshape(pool, 4 * P)],
+                           axis=1)
+    q8 = _to_e4m3fn_bytes(rng.standard_normal((B, H, D)).astype(np.float32))
+    w = (rng.standard_normal((B, H)) / 8.0).astype(np.float32)
+    print(f"\n[parity] indexer rounds: B={B} keys {int(lens.sum())}", flush=True)
+    batch = dsa.make_batch(torch.from_numpy(bt).cuda(), torch.from_numpy(lens).cuda(), page_size=P,
+                           num_pages=pool, max_seq_len_k=max_len)
+    logits = torch.empty((B, max_len), dtype=torch.float32, device="cuda")
+    dsa.dsa_indexer_logits(batch, torch.from_numpy(q8).cuda(), torch.from_numpy(w).cuda(),
+                           torch.from_numpy(cache).cuda(), logits)
+    torch.cuda.synchronize()
+    wl = types.SimpleNamespace(q_idx=q8, w=w, index_cache=cache, block_table=bt, seq_lens_k=lens,
+                               cu_seqlens_q=None, cfg=types.SimpleNamespace(page_size=P, idx_kind="fp8"))
+    rows = sorted({0, 1, 511, 1022, 1023, int(np.argmax(lens))})
+    _, worst = parity.check_logits(logits.cpu().numpy(), wl, rows)
+    print(f"[parity] indexer rounds: rows {rows} logits err/bound {worst:.3f}", flush=True)
+
+
 def test_empty_batch_launches_nothing():
     _need_gpu()
     import sparse_mla_attention_dsa_amd as dsa
