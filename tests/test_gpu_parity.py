@@ -124,18 +124,20 @@ def test_full_prefill_sampled():
     _full_check(CONFIGS["prefill_4k_on_16k"], rows=[0, 1, 2047, 4094, 4095])
 
 
-def test_indexer_chunk_records_in_rounds():
-    """1,024 decode rows of 15-20k keys over a shared pool of 320 pages (rows
-    may name the same page, as shared prefixes do): every work-group of the
-    stream indexer owns more chunks than its LDS record table holds (1,024)
-    and takes them in two rounds. Sampled rows against the oracle."""
+def _shared_pool_indexer(seed, lens, q_lens=None, pool=320, check_rows=()):
+    """The fp8 indexer on rows whose block tables name pages of one shared pool
+    (as shared prefixes do), so that large batches need little memory; the
+    listed rows (and the first, last and longest) against the oracle."""
     _need_gpu()
     import types
     import sparse_mla_attention_dsa_amd as dsa
     from dsa_workloads import _to_e4m3fn_bytes
-    rng = np.random.default_rng(620)
-    B, P, pool, H, D = 1024, 64, 320, 64, 128
-    lens = rng.integers(15000, 20001, size=B).astype(np.int32)
+    rng = np.random.default_rng(seed)
+    P, H, D = 64, 64, 128
+    lens = np.asarray(lens, dtype=np.int32)
+    B = len(lens)
+    cu = None if q_lens is None else np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    T = B if cu is None else int(cu[-1])
     max_len = int(lens.max())
     bt = rng.integers(0, pool, size=(B, -(-max_len // P))).astype(np.int32)
     keys = rng.standard_normal((pool * P, D)).astype(np.float32)
@@ -143,20 +145,47 @@ def test_indexer_chunk_records_in_rounds():
     codes = _to_e4m3fn_bytes(keys / sig[:, None])
     cache = np.concatenate([codes.reshape(pool, P * D), sig.reshape(pool, P).view(np.uint8).reshape(pool, 4 * P)],
                            axis=1)
-    q8 = _to_e4m3fn_bytes(rng.standard_normal((B, H, D)).astype(np.float32))
-    w = (rng.standard_normal((B, H)) / 8.0).astype(np.float32)
-    print(f"\n[parity] indexer rounds: B={B} keys {int(lens.sum())}", flush=True)
-    batch = dsa.make_batch(torch.from_numpy(bt).cuda(), torch.from_numpy(lens).cuda(), page_size=P,
-                           num_pages=pool, max_seq_len_k=max_len)
-    logits = torch.empty((B, max_len), dtype=torch.float32, device="cuda")
+    q8 = _to_e4m3fn_bytes(rng.standard_normal((T, H, D)).astype(np.float32))
+    w = (rng.standard_normal((T, H)) / 8.0).astype(np.float32)
+    print(f"\n[parity] shared-pool indexer: {B} requests, {T} rows, keys {int(lens.sum())}", flush=True)
+    batch = dsa.make_batch(torch.from_numpy(bt).cuda(), torch.from_numpy(lens).cuda(),
+                           None if cu is None else torch.from_numpy(cu).cuda(), page_size=P, num_pages=pool,
+                           max_seq_len_k=max_len, max_seq_len_q=1 if q_lens is None else int(max(q_lens)),
+                           num_rows=T)
+    logits = torch.empty((T, max_len), dtype=torch.float32, device="cuda")
     dsa.dsa_indexer_logits(batch, torch.from_numpy(q8).cuda(), torch.from_numpy(w).cuda(),
                            torch.from_numpy(cache).cuda(), logits)
     torch.cuda.synchronize()
     wl = types.SimpleNamespace(q_idx=q8, w=w, index_cache=cache, block_table=bt, seq_lens_k=lens,
-                               cu_seqlens_q=None, cfg=types.SimpleNamespace(page_size=P, idx_kind="fp8"))
-    rows = sorted({0, 1, 511, 1022, 1023, int(np.argmax(lens))})
+                               cu_seqlens_q=cu, cfg=types.SimpleNamespace(page_size=P, idx_kind="fp8"))
+    longest = int(np.argmax(lens)) if cu is None else int(cu[int(np.argmax(lens)) + 1]) - 1
+    rows = sorted({0, T - 1, longest, *check_rows})
     _, worst = parity.check_logits(logits.cpu().numpy(), wl, rows)
-    print(f"[parity] indexer rounds: rows {rows} logits err/bound {worst:.3f}", flush=True)
+    print(f"[parity] shared-pool indexer: rows {rows} logits err/bound {worst:.3f}", flush=True)
+
+
+def test_indexer_chunk_records_in_rounds():
+    """1,024 decode rows of 15-20k keys: every work-group of the stream
+    indexer owns more chunks than its LDS record table holds (1,024) and takes
+    them in two rounds."""
+    lens = np.random.default_rng(620).integers(15000, 20001, size=1024)
+    _shared_pool_indexer(620, lens, check_rows=(1, 511, 1022))
+
+
+def test_indexer_more_rows_than_stream_units():
+    """1,100 decode rows (more than the stream kernel's 1,024 units): the
+    general fp8 kernel, one work-group per (row, 512 keys)."""
+    lens = np.random.default_rng(621).integers(1, 3001, size=1100)
+    _shared_pool_indexer(621, lens, check_rows=(7, 1024, 1025))
+
+
+def test_indexer_more_requests_than_prefill_blocks():
+    """1,030 two-row requests (more than the two-row stream kernel's 512 and
+    the prefill kernel's 1,024 requests): the general fp8 kernel with causal
+    visible lengths per row."""
+    rng = np.random.default_rng(622)
+    lens = rng.integers(2, 2500, size=1030)
+    _shared_pool_indexer(622, lens, q_lens=[2] * 1030, check_rows=(2, 3, 2057))
 
 
 def test_empty_batch_launches_nothing():
