@@ -120,6 +120,14 @@ def test_full_ragged_batch64_fp8_cache_sampled():
     _full_check(cfg, rows=rows)
 
 
+def test_decode_batch32_four_splits_sampled():
+    """32 decode rows: the attention plans four splits per row (the unrolled
+    four-way merge), bf16 and fp8 latent caches."""
+    lens = [int(x) for x in np.random.default_rng(118).integers(2049, 4000, size=32)]
+    for kind, seed in (("bf16", 118), ("fp8", 119)):
+        _full_check(small_config(f"dec32_{kind}", seed=seed, lens=lens, mla_kind=kind), rows=[0, 13, 31])
+
+
 def test_full_prefill_sampled():
     _full_check(CONFIGS["prefill_4k_on_16k"], rows=[0, 1, 2047, 4094, 4095])
 
