@@ -95,7 +95,7 @@ typedef struct {
   int32_t page_size;         /* P: tokens per page, a positive multiple of 16 */
   int32_t max_pages_per_seq; /* row stride of block_table, >= 1 */
   int32_t num_pages;         /* pages in each cache pool; page ids outside [0, num_pages) are absent */
-  int32_t max_seq_len_k;     /* host: >= every seq_lens_k[b]; sizes grids, never read back */
+  int32_t max_seq_len_k;     /* host: >= every seq_lens_k[b], at most 2^24; sizes grids, never read back */
   int32_t max_seq_len_q;     /* host: >= every q_len_b (1 for decode) */
   const int32_t *block_table;  /* [B, max_pages_per_seq] physical page ids */
   const int32_t *seq_lens_k;   /* [B] keys in the cache, this step's tokens included */

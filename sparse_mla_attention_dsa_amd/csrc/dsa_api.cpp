@@ -51,6 +51,10 @@ dsa_status_t check_batch(const dsa_batch_t* batch, BatchView* bv) {
   if ((int64_t)b.max_pages_per_seq * b.page_size > INT32_MAX)
     return fail(DSA_ERR_UNSUPPORTED, "max_pages_per_seq * page_size exceeds 2^31 - 1 positions");
   if (b.max_seq_len_k < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "max_seq_len_k %d < 0", b.max_seq_len_k);
+  // 2^24 keys per row keeps every key and group count of a launch (up to 1024
+  // rows in one stream launch) and every grid dimension inside 32 bits
+  if (b.max_seq_len_k > (1 << 24))
+    return fail(DSA_ERR_UNSUPPORTED, "max_seq_len_k %d exceeds 2^24", b.max_seq_len_k);
   if (b.max_seq_len_q < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "max_seq_len_q %d < 0", b.max_seq_len_q);
   if (b.num_seqs > 0 && (!b.block_table || !b.seq_lens_k))
     return fail(DSA_ERR_INVALID_ARGUMENT, "block_table / seq_lens_k is NULL");

@@ -90,6 +90,11 @@ def test_topk_rejects_bad_k(L, k):
     assert _idx(L, _batch(), k=k) == dsa.DSA_ERR_INVALID_ARGUMENT
 
 
+def test_contexts_beyond_2_pow_24_are_unsupported(L):
+    assert _idx(L, _batch(max_seq_len_k=(1 << 24) + 1)) == dsa.DSA_ERR_UNSUPPORTED
+    assert _logits(L, _batch(max_seq_len_k=(1 << 24) + 1), stride=(1 << 24) + 1) == dsa.DSA_ERR_UNSUPPORTED
+
+
 def test_null_batch(L):
     assert L.dsa_topk(None, None, 1, 1, None, None, 0, None) == dsa.DSA_ERR_INVALID_ARGUMENT
 
