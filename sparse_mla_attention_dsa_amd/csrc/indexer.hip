@@ -163,9 +163,10 @@ constexpr int kStreamMaxUnits = 1024;
 constexpr int kStreamBatch = 4;                                  // groups per chunk
 constexpr int kStreamMaxQLen = 4;                                // rows per request, multi-row units
 constexpr int kStreamMaxChunks = 1024;                           // chunk records per round
+constexpr int kDecodeAhead = 1;                                  // chunks in flight per wave (decode)
 
 // Waves per work-group: as many as the registers let one CU hold
-template <int kR> constexpr int stream_waves() { return kR == 1 ? 12 : 8; }
+template <int kR, int kAhead> constexpr int stream_waves() { return kR == 1 && kAhead == 1 ? 12 : 8; }
 
 // Unit u of a stream launch with kR rows per unit. kR = 1: unit u is decode
 // row u. kR = 2: unit u is rows 2 (u & 1) and 2 (u & 1) + 1 of request u >> 1
@@ -199,9 +200,9 @@ __device__ __forceinline__ int stream_chunks(int n, int gpp, int cpp) {
   return (n / gpp) * cpp + (n % gpp + kStreamBatch - 1) / kStreamBatch;
 }
 
-template <int kR>
-__global__ __launch_bounds__(stream_waves<kR>() * kWave) void indexer_fp8_stream_kernel(IndexerParams p) {
-  constexpr int kWaves = stream_waves<kR>();
+template <int kR, int kAhead>
+__global__ __launch_bounds__((stream_waves<kR, kAhead>() * kWave)) void indexer_fp8_stream_kernel(IndexerParams p) {
+  constexpr int kWaves = stream_waves<kR, kAhead>();
   constexpr int kThreads = kWaves * kWave;
   __shared__ int pre[kStreamMaxUnits + 1];                       // chunk prefix over units
   __shared__ int wsum[kWaves];
@@ -339,25 +340,24 @@ __global__ __launch_bounds__(stream_waves<kR>() * kWave) void indexer_fp8_stream
     __syncthreads();
 
     // ---- the waves take chunks until the round is done: a wave holds the
-    // chunk it computes (its keys loaded) and the next one (loads issued
-    // before the MFMAs), and takes the one after during the MFMAs ----
-    i32x8 kb[2][kStreamBatch];
-    float sg[2][kStreamBatch];
-    int j = take();
-    Batch cur = {};
-    if (j < n) {
-      cur = record(j);
-      load_batch(cur, kb[0], sg[0]);
-    }
-    int jn = j < n ? take() : n;
-    while (j < n) {
-      Batch nx = {};
-      if (jn < n) {
-        nx = record(jn);
-        load_batch(nx, kb[1], sg[1]);
+    // chunk it computes and the kAhead after it (their loads in flight during
+    // the MFMAs), and takes the next one during the MFMAs ----
+    i32x8 kb[kAhead + 1][kStreamBatch];
+    float sg[kAhead + 1][kStreamBatch];
+    Batch bq[kAhead + 1] = {};
+    int jq[kAhead + 1];
+#pragma unroll
+    for (int d = 0; d <= kAhead; ++d) {
+      jq[d] = (d == 0 || jq[d - 1] < n) ? take() : n;
+      if (jq[d] < n) {
+        bq[d] = record(jq[d]);
+        load_batch(bq[d], kb[d], sg[d]);
       }
-      int jnn = n;                                               // read after the MFMAs
-      if (lane == 0 && jn < n) jnn = atomicAdd(&next_chunk, 1);
+    }
+    while (jq[0] < n) {
+      int jt = n;                                                // read after the MFMAs
+      if (lane == 0 && jq[kAhead] < n) jt = atomicAdd(&next_chunk, 1);
+      const Batch cur = bq[0];
       if (cur.t != q_unit) load_unit(cur);
       // ---- logits of the chunk, for every row of its unit ----
       const bool okp = cur.page >= 0 && cur.page < bv.num_pages;
@@ -384,11 +384,19 @@ __global__ __launch_bounds__(stream_waves<kR>() * kWave) void indexer_fp8_stream
           if (g == 0 && s < vis) out[s] = okp ? part * sg[0][u] : -INFINITY;
         }
       }
-      cur = nx;
+      const int tail = jq[kAhead];
 #pragma unroll
-      for (int u = 0; u < kStreamBatch; ++u) { kb[0][u] = kb[1][u]; sg[0][u] = sg[1][u]; }
-      j = jn;
-      jn = jn < n ? __builtin_amdgcn_readfirstlane(jnn) : n;
+      for (int d = 0; d < kAhead; ++d) {
+        bq[d] = bq[d + 1];
+        jq[d] = jq[d + 1];
+#pragma unroll
+        for (int u = 0; u < kStreamBatch; ++u) { kb[d][u] = kb[d + 1][u]; sg[d][u] = sg[d + 1][u]; }
+      }
+      jq[kAhead] = tail < n ? __builtin_amdgcn_readfirstlane(jt) : n;
+      if (jq[kAhead] < n) {
+        bq[kAhead] = record(jq[kAhead]);
+        load_batch(bq[kAhead], kb[kAhead], sg[kAhead]);
+      }
     }
     __syncthreads();                                             // records free for the next round
   }
@@ -709,7 +717,7 @@ __global__ __launch_bounds__(kF32Block) void indexer_f32_kernel(IndexerParams p)
 // Work-groups of a stream kernel that the current device holds at once: CUs
 // times the occupancy the kernel's registers and LDS allow (one per CU).
 // Queried once per device and kernel (host calls only, nothing is enqueued).
-template <int kR>
+template <int kR, int kAhead>
 int resident_wgs() {
   constexpr int kMaxDevices = 64;
   static std::atomic<int> cache[kMaxDevices];
@@ -721,8 +729,8 @@ int resident_wgs() {
   }
   int cus = 0, per_cu = 0;
   if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, indexer_fp8_stream_kernel<kR>,
-                                                   stream_waves<kR>() * kWave, 0) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, indexer_fp8_stream_kernel<kR, kAhead>,
+                                                   stream_waves<kR, kAhead>() * kWave, 0) != hipSuccess ||
       cus < 1 || per_cu < 1) {
     (void)hipGetLastError();
     return 256;                                                  // MI355X: 256 CUs
@@ -771,17 +779,17 @@ hipError_t launch_indexer_fp8(const IndexerParams& p, hipStream_t s) {
     // once (one round: a second round would start late and finish last)
     const int64_t units = decode ? p.batch.num_rows : std::min<int64_t>(p.batch.num_rows, 2LL * p.batch.num_seqs);
     const int64_t chunks = units * ((p.batch.max_seq_len_k + 16 * kStreamBatch - 1) / (16 * kStreamBatch));
-    const int waves = decode ? stream_waves<1>() : stream_waves<2>();
+    const int waves = decode ? stream_waves<1, kDecodeAhead>() : stream_waves<2, 1>();
     int64_t wgs = (chunks + waves - 1) / waves;
-    const int resident = decode ? resident_wgs<1>() : resident_wgs<2>();
+    const int resident = decode ? resident_wgs<1, kDecodeAhead>() : resident_wgs<2, 1>();
     if (wgs > resident) wgs = resident;
     if (wgs < 1) wgs = 1;
     if (decode)
-      hipLaunchKernelGGL(HIP_KERNEL_NAME(indexer_fp8_stream_kernel<1>), dim3((unsigned)wgs),
-                         dim3(stream_waves<1>() * kWave), 0, s, p);
+      hipLaunchKernelGGL(HIP_KERNEL_NAME(indexer_fp8_stream_kernel<1, kDecodeAhead>), dim3((unsigned)wgs),
+                         dim3(stream_waves<1, kDecodeAhead>() * kWave), 0, s, p);
     else
-      hipLaunchKernelGGL(HIP_KERNEL_NAME(indexer_fp8_stream_kernel<2>), dim3((unsigned)wgs),
-                         dim3(stream_waves<2>() * kWave), 0, s, p);
+      hipLaunchKernelGGL(HIP_KERNEL_NAME(indexer_fp8_stream_kernel<2, 1>), dim3((unsigned)wgs),
+                         dim3(stream_waves<2, 1>() * kWave), 0, s, p);
     return hipGetLastError();
   }
   if (p.batch.cu_seqlens_q != nullptr && p.batch.num_seqs <= kPfMaxSeqs && p.stride <= kPfMaxStride) {
