@@ -68,6 +68,23 @@ __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
   return __shfl_xor(v, mask, kWave);
 }
 
+// max / sum of v over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 16-lane
+// groups), with the gfx950 lane swaps (VALU, no LDS round trip); every lane
+// gets the result
+__device__ __forceinline__ float max_over_groups(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float sum_over_groups(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave, on DPP lane moves (no LDS
 // round trip): shifts of 1, 2, 4, 8 lanes inside each 16-lane row, then the
 // last lane of row 0 / row 2 is added to rows 1 / 3, and the last lane of

@@ -46,14 +46,6 @@ __device__ __forceinline__ float relu_bits(float x) {
   return __int_as_float(max(__float_as_int(x), 0));
 }
 
-// sum of v over lanes l, l ^ 16, l ^ 32, l ^ 48, with the gfx950 lane swaps (VALU, no LDS)
-__device__ __forceinline__ float sum_over_groups(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 __global__ __launch_bounds__(64 * kIdxWaves) void indexer_fp8_kernel(IndexerParams p) {
   __shared__ i32x8 q_lds[kIdxHeads * kIdxDim / 32];   // the row's q, 8 KB
   const BatchView& bv = p.batch;
@@ -137,8 +129,7 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_fp8_kernel(IndexerPara
 #pragma unroll
       for (int i = 0; i < 4; ++i) part = fmaf(wv[4 * m + i], relu_bits(acc[i]), part);
     }
-    part += shfl_xor_f(part, 16);
-    part += shfl_xor_f(part, 32);
+    part = sum_over_groups(part);
     const int s = s0 + c;
     if (g == 0 && s < k_end) out[s] = ok[u] ? part * sig[u] : -INFINITY;
   }
@@ -378,8 +369,7 @@ __global__ __launch_bounds__((stream_waves<kR, kAhead>() * kWave)) void indexer_
 #pragma unroll
             for (int i = 0; i < 4; ++i) part = fmaf(wv[r][4 * m + i], relu_bits(acc[i]), part);
           }
-          part += shfl_xor_f(part, 16);
-          part += shfl_xor_f(part, 32);
+          part = sum_over_groups(part);
           const int s = 16 * (cur.gi + u) + c;
           if (g == 0 && s < vis) out[s] = okp ? part * sg[0][u] : -INFINITY;
         }

@@ -76,20 +76,6 @@ struct F8Shared {
 
 __device__ __forceinline__ int swz8(int row) { return (row >> 2) & 3; }
 
-__device__ __forceinline__ float max_over_groups8(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
-__device__ __forceinline__ float sum_over_groups8(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 __device__ __forceinline__ f32x4 mfma_fp8_k128(const i32x8& a, const i32x8& b, const f32x4& c) {
   // format 0 = E4M3 for both operands, no block scales (the unscaled form)
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
@@ -327,7 +313,7 @@ __global__ __launch_bounds__(kF8Threads) void mla_fp8_kernel(MlaParams p) {
           sv[4 * rb + i] = v;
           mx = fmaxf(mx, v);
         }
-      mx = max_over_groups8(mx);
+      mx = max_over_groups(mx);
       *alpha = 1.f;
       if (mx > m_ref + kF8RescaleThreshold) {
         *alpha = __builtin_amdgcn_exp2f(m_ref - mx);
@@ -388,7 +374,7 @@ __global__ __launch_bounds__(kF8Threads) void mla_fp8_kernel(MlaParams p) {
       wait_tiles8(min(tile + kAhead, last) - (tile + 2), five);
       __syncthreads();                                 // B2
     }
-    const float l = sum_over_groups8(l_part);
+    const float l = sum_over_groups(l_part);
     if (g == 0) {
       const float lse_val = (l > 0.f) ? (m_ref + log2f(l)) * kF8Ln2 : -INFINITY;
       if (S == 1) {
