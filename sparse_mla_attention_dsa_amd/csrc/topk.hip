@@ -403,9 +403,12 @@ int topk_chunk(int num_rows, int max_len, int k) {
   // the rows are longer than the LDS key cache (a whole-row work-group would
   // re-read them from L2 in every pass; for cached rows one phase is faster,
   // measured). The candidates of a row (chunks x k) must fit the merge's LDS
-  // key cache, and a chunk its own.
+  // key cache, and a chunk its own. Chunks start at 16384 positions: both
+  // phases are dominated by the fixed cost of a selection, and 16384 beats
+  // 8192 (more, shorter phase-one selections and twice the candidates) and
+  // 32768 on the 8 x 128k decode (34.6 against 38.7 and 35.5 us, measured).
   if (num_rows > 256 || k > kTkCache / 2 || max_len <= kTkCache) return 0;
-  int chunk = 8192;
+  int chunk = 16384;
   if (chunk < 2 * k) chunk = 2 * k;
   const int64_t need = ((int64_t)max_len * k + kTkCache - 1) / kTkCache;   // chunks * k <= kTkCache
   while (chunk < need) chunk *= 2;

@@ -193,8 +193,8 @@ def test_attention_rejects_misaligned_pointers(L, fp8, which):
 def test_topk_workspace_for_few_long_rows(L):
     few_long = _batch(num_seqs=8, num_rows=8, max_pages_per_seq=2048, max_seq_len_k=131072)
     need = L.dsa_workspace_bytes(dsa.DSA_OP_TOPK, ctypes.byref(few_long), 2048, 0, 0, 0)
-    # 16 chunks of 8192 per row, 2048 (key, position) candidates of 8 bytes each
-    assert need == 8 * 16 * 2048 * 8
+    # 8 chunks of 16384 per row, 2048 (key, position) candidates of 8 bytes each
+    assert need == 8 * 8 * 2048 * 8
     assert _idx(L, few_long, stride=131072) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
     many = _batch(num_seqs=4096, num_rows=4096, max_pages_per_seq=2048, max_seq_len_k=131072)
     assert L.dsa_workspace_bytes(dsa.DSA_OP_TOPK, ctypes.byref(many), 2048, 0, 0, 0) == 0
