@@ -621,7 +621,10 @@ int mla_bf16_splits(int num_rows, int k, int heads) {
   if (groups <= 0) return 1;
   const int min_splits = (k + kMlaMaxEntriesPerBlock - 1) / kMlaMaxEntriesPerBlock;
   int max_splits = (k + 2 * kMlaTile - 1) / (2 * kMlaTile);         // >= 2 tiles per split
-  if (max_splits > 16) max_splits = 16;
+  // at most 8: for few rows, longer splits cost less in prologues and merge
+  // than the idle CUs they leave (measured on the batch-1 and batch-8 decodes:
+  // 8 beats 4, 16 and 32)
+  if (max_splits > 8) max_splits = 8;
   int sp = (256 + groups - 1) / groups;
   if (sp > max_splits) sp = max_splits;
   if (sp < min_splits) sp = min_splits;
