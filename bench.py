@@ -1,6 +1,6 @@
 """Benchmark of one DSA decode step (indexer -> top-k -> sparse MLA) on one GPU.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--extra-workloads A,B]
 
 A step is one pass of the whole hot path over one batch: dsa_indexer_logits,
 dsa_topk and sparse_mla_decode (with its split-KV combine) on one stream. The
@@ -9,8 +9,11 @@ resident. Prints one JSON line:
 
 * value: decode tokens/s = rows per step / step time (one token per request);
 * sparse_attn_hbm_gbps: algorithmic sparse-attention bytes / attention time;
-* roofline: the dominant kernel's algorithmic bytes (or FLOPs) per launch over
-  its average launch time, against the MI355X peak;
+* roofline: the dominant kernel's algorithmic bytes (or FLOPs, when its FLOP
+  per byte is above the MFMA ridge) per launch over its average launch time,
+  against the MI355X peak;
+* extra: the same step on further workloads (by default the batch-64 decode
+  with every context at 32,768 keys, the literal "ctx 32k" of the metric);
 * cpu_baseline: the float64 oracle timed on a bounded sample of the same
   workload on this host's cores.
 """
@@ -29,35 +32,90 @@ METRIC = "decode tokens/s + sparse-attn HBM GB/s, 1 GPU, ctx 32k, top-k 2048"
 HBM_PEAK_GBPS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP32_PEAK_TFLOPS = 157.3
+
+
+def visible_lengths(seq_lens_k, cu_seqlens_q):
+    """Keys each query row sees: a decode row its whole request; the j-th of a
+    request's q_len rows seq_len - q_len + j + 1 (bottom-right causal)."""
+    lens = np.asarray(seq_lens_k, dtype=np.int64)
+    if cu_seqlens_q is None:
+        return np.maximum(lens, 0), np.arange(len(lens))
+    cu = np.asarray(cu_seqlens_q, dtype=np.int64)
+    q_lens = np.diff(cu)
+    seq = np.repeat(np.arange(len(lens)), q_lens)
+    j = np.arange(int(cu[-1])) - np.repeat(cu[:-1], q_lens)
+    vis = lens[seq] - q_lens[seq] + j + 1
+    return np.maximum(vis, 0), seq
+
+
+def _bound(flops, nbytes, mfma_peak_tflops):
+    """The roofline a stage sits under: MFMA when its FLOP per byte is above
+    the ridge of its MFMA dtype, HBM otherwise."""
+    ridge = mfma_peak_tflops * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    return "mfma" if flops and flops / max(nbytes, 1) > ridge else "hbm"
 
 
 def algorithmic_work(wl):
-    """Bytes and FLOPs each stage must move/compute at minimum (per step)."""
+    """Bytes and FLOPs each stage must move or compute at minimum (per step).
+
+    * indexer: every index key a request's rows see is read once per request
+      (its rows share the read), 132 B per key for fp8 x 128 + fp32 scale;
+      each row reads its q and gates and writes 4 B per visible logit;
+      2 H D FLOP per (row, visible key).
+    * top-k: each row reads its visible logits (4 B each) and writes k indices.
+    * sparse MLA: each selected row is gathered once per query row that
+      selects it (1,152 B for bf16 576-wide rows); decode rows of different
+      requests share nothing, so this is HBM traffic. Rows of one request
+      (prefill, multi-token decode) select overlapping sets out of at most
+      seq_len cached rows, so HBM traffic is counted as the distinct rows
+      (at most seq_len per request) and the per-row gather is reported
+      separately as cache-served traffic. Plus q, out, indices and lse.
+      FLOPs: Hm (2 (Dl + Dr) + 2 Dl) per selected (row, head-independent entry).
+    """
     cfg = wl.cfg
-    import oracle  # row layout only (visible lengths)
-    rows = oracle.row_layout(wl.seq_lens_k, wl.cu_seqlens_q)
-    vis = np.array([r.visible for r in rows], dtype=np.int64)
+    vis, seq = visible_lengths(wl.seq_lens_k, wl.cu_seqlens_q)
+    T = len(vis)
     H, D, k = cfg.idx_heads, cfg.idx_dim, cfg.topk
     esize = 1 if cfg.idx_kind == "fp8" else 4
     key_bytes = D * esize + 4                       # 132 B for fp8 x 128 + fp32 scale
-    idx_bytes = int(vis.sum()) * (key_bytes + 4) + len(vis) * (H * D * esize + 4 * H)
+    per_req_keys = np.zeros(len(wl.seq_lens_k), dtype=np.int64)
+    np.maximum.at(per_req_keys, seq, vis)
+    idx_bytes = (int(per_req_keys.sum()) * key_bytes + int(vis.sum()) * 4
+                 + T * (H * D * esize + 4 * H))
     idx_flops = int(vis.sum()) * 2 * H * D
-    topk_bytes = int(vis.sum()) * 4 + len(vis) * 4 * k
+    topk_bytes = int(vis.sum()) * 4 + T * 4 * k
     sel = np.minimum(vis, k)
     Hm, Dl, Dr = cfg.mla_heads, cfg.d_latent, cfg.d_rope
     msize = {"bf16": 2, "fp8": 1}.get(cfg.mla_kind, 4)          # cached row and query element
     osize = 4 if cfg.mla_kind == "f32" else 2                    # output element (bf16 for fp8 too)
     row_bytes = (Dl + Dr) * msize
-    mla_bytes = int(sel.sum()) * row_bytes + len(vis) * (Hm * (Dl + Dr) * msize + Hm * Dl * osize
-                                                         + 4 * k + 4 * Hm)
+    per_row_io = Hm * (Dl + Dr) * msize + Hm * Dl * osize + 4 * k + 4 * Hm
+    gathered = int(sel.sum()) * row_bytes
+    if wl.cu_seqlens_q is None:
+        distinct = int(sel.sum())
+    else:
+        per_req_sel = np.zeros(len(wl.seq_lens_k), dtype=np.int64)
+        np.add.at(per_req_sel, seq, sel)
+        distinct = int(np.minimum(per_req_sel, np.asarray(wl.seq_lens_k, dtype=np.int64)).sum())
+    mla_bytes = distinct * row_bytes + T * per_row_io
     mla_flops = int(sel.sum()) * Hm * (2 * (Dl + Dr) + 2 * Dl)
+    idx_peak = FP8_PEAK_TFLOPS if cfg.idx_kind == "fp8" else FP32_PEAK_TFLOPS
+    mla_peak = {"bf16": BF16_PEAK_TFLOPS, "fp8": FP8_PEAK_TFLOPS}.get(cfg.mla_kind, FP32_PEAK_TFLOPS)
     return {
-        "indexer": {"bytes": idx_bytes, "flops": idx_flops, "per_unit": f"{key_bytes + 4} B per visible key "
-                    f"(+{H * D * esize + 4 * H} B per row)", "units": int(vis.sum())},
-        "topk": {"bytes": topk_bytes, "flops": 0, "per_unit": f"4 B per visible score (+{4 * k} B per row)",
-                 "units": int(vis.sum())},
-        "sparse_mla": {"bytes": mla_bytes, "flops": mla_flops,
-                       "per_unit": f"{row_bytes} B per selected row (+{Hm * (Dl + Dr) * msize + Hm * Dl * osize + 4 * k + 4 * Hm} B per query row)",
+        "indexer": {"bytes": idx_bytes, "flops": idx_flops, "peak_tflops": idx_peak,
+                    "bound": _bound(idx_flops, idx_bytes, idx_peak),
+                    "per_unit": f"{key_bytes} B per key of a request (read once for its rows) + 4 B per "
+                                f"(row, visible key) logit + {H * D * esize + 4 * H} B per row; "
+                                f"{2 * H * D} FLOP per (row, visible key)",
+                    "units": int(vis.sum())},
+        "topk": {"bytes": topk_bytes, "flops": 0, "peak_tflops": None, "bound": "hbm",
+                 "per_unit": f"4 B per visible score (+{4 * k} B per row)", "units": int(vis.sum())},
+        "sparse_mla": {"bytes": mla_bytes, "flops": mla_flops, "peak_tflops": mla_peak,
+                       "bound": _bound(mla_flops, mla_bytes, mla_peak),
+                       "gather_bytes": gathered + T * per_row_io,
+                       "per_unit": f"{row_bytes} B per distinct selected cache row (+{per_row_io} B per "
+                                   f"query row); {Hm * (2 * (Dl + Dr) + 2 * Dl)} FLOP per selected entry",
                        "units": int(sel.sum())},
     }
 
@@ -131,7 +189,32 @@ def cpu_baseline(wl, budget_s=12.0, max_rows=4096):
     el = time.perf_counter() - t0
     return {"value": done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} decode rows (rows 0.. of the {wl.num_rows}-row batch, cycling), all three "
-                      f"stages per row (float64 numpy), {el:.1f} s"}
+                      f"stages per row (float64 numpy), {el:.1f} s",
+            "cpu_model": _cpu_model(), "blas": _blas_vendor(),
+            "host_cores_available": len(os.sched_getaffinity(0))}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _blas_vendor():
+    """numpy's BLAS library as threadpoolctl reports it (name, version, threads)."""
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                return f"{i.get('internal_api')} {i.get('version')} ({i.get('num_threads')} threads)"
+    except Exception:
+        pass
+    return None
 
 
 def copy_calibration(mib):
@@ -147,34 +230,21 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n}))
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode_b64_ragged")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-graph", action="store_true", help="launch the timed steps eagerly")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="only run a plain device-to-device copy of MIB mebibytes (counter calibration)")
-    args = ap.parse_args()
+def measure(cfg, K, W, graph=True, with_input_side=True):
+    """Generate `cfg`, run W eager warm-up steps, time K steps, time the stages.
 
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
-        return
-
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the DSA step is not "
-              "sharded across GPUs in this library", file=sys.stderr)
-        sys.exit(2)
-
+    The K timed steps are one HIP graph (captured once, replayed once), as a
+    serving loop would run them: host launch overhead is not part of the step.
+    The per-stage times come from a second pass of K eager steps with events
+    recorded on the stream between the stages; a GPU spin queued in front lets
+    the host enqueue the whole pass first, so the kernels run back to back
+    (same order, same data, same cache state) and each event pair brackets one
+    stage's kernels."""
     import torch
 
-    from dsa_workloads import CONFIGS, generate
+    from dsa_workloads import generate
     from dsa_workloads.device import make_step
 
-    cfg = CONFIGS[args.workload]
     t_gen = time.perf_counter()
     wl = generate(cfg)
     print(f"[bench] generated {cfg.name} in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
@@ -182,23 +252,14 @@ def main():
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
-    for _ in range(args.warmup):
+    for _ in range(W):
         step.run()
     torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    print(f"[bench] {cfg.name}: warmup done ({W} steps)", file=sys.stderr, flush=True)
 
-    # The K timed steps are one HIP graph (captured once, replayed once), as a
-    # serving loop would run them: host launch overhead is not part of the
-    # step. The per-stage times come from a second pass of K eager steps with
-    # events recorded on the stream between the stages; a GPU spin queued in
-    # front lets the host enqueue the whole pass first, so the kernels run back
-    # to back (same order, same data, same cache state) and each event pair
-    # brackets one stage's kernels.
-    K = args.steps
     stages = (("indexer", step.indexer), ("topk", step.select), ("sparse_mla", step.attend))
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    stream = torch.cuda.current_stream()
-    if args.no_graph:
+    if not graph:
         run_all = lambda: [step.run() for _ in range(K)]
     else:
         side = torch.cuda.Stream()
@@ -219,8 +280,7 @@ def main():
     run_all()
     end.record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / K
+    ms_per_step = start.elapsed_time(end) / K
 
     try:
         torch.cuda._sleep(40_000_000)                        # ~20 ms of GPU spin
@@ -235,18 +295,18 @@ def main():
     torch.cuda.synchronize()
     stage_ms = {name: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev]))
                 for j, (name, _) in enumerate(stages)}
-    print(f"[bench] timed {K} steps: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+    print(f"[bench] {cfg.name}: timed {K} steps: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
 
-    input_side = time_input_side(wl, K, stream)
+    input_side = time_input_side(wl, K, stream) if with_input_side else None
 
     work = algorithmic_work(wl)
-    tokens_per_s = wl.num_rows / (ms_per_step * 1e-3)
     kernels = {}
     for name, w in work.items():
         t_s = stage_ms[name] * 1e-3
         gbps = w["bytes"] / t_s / 1e9
         kernels[name] = {
             "us": stage_ms[name] * 1e3,
+            "bound": w["bound"],
             "algorithmic_bytes": w["bytes"],
             "algorithmic_flops": w["flops"],
             "hbm_gbps": gbps,
@@ -254,10 +314,13 @@ def main():
             "per_unit": w["per_unit"],
             "units": w["units"],
         }
+        if "gather_bytes" in w and w["gather_bytes"] != w["bytes"]:
+            kernels[name]["gather_bytes"] = w["gather_bytes"]
+            kernels[name]["gather_gbps"] = w["gather_bytes"] / t_s / 1e9
         if w["flops"]:
-            peak = FP8_PEAK_TFLOPS if name == "indexer" and cfg.idx_kind == "fp8" else BF16_PEAK_TFLOPS
             kernels[name]["tflops"] = w["flops"] / t_s / 1e12
-            kernels[name]["mfma_frac"] = kernels[name]["tflops"] / peak
+            kernels[name]["mfma_peak_tflops"] = w["peak_tflops"]
+            kernels[name]["mfma_frac"] = kernels[name]["tflops"] / w["peak_tflops"]
     dominant = max(stage_ms, key=stage_ms.get)
     dk = kernels[dominant]
     traffic = None
@@ -270,17 +333,59 @@ def main():
                 traffic = rec["bytes_per_launch"]
         except Exception:
             traffic = None
-    roofline = {"kernel": dominant, "bound": "hbm", "achieved": dk["hbm_gbps"], "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": dk["hbm_frac"], "traffic": traffic}
+    if dk["bound"] == "mfma":
+        roofline = {"kernel": dominant, "bound": "mfma", "achieved": dk["tflops"], "peak": dk["mfma_peak_tflops"],
+                    "unit": "TFLOP/s", "frac": dk["mfma_frac"], "traffic": traffic}
+    else:
+        roofline = {"kernel": dominant, "bound": "hbm", "achieved": dk["hbm_gbps"], "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": dk["hbm_frac"], "traffic": traffic}
+    return wl, {
+        "tokens_per_s": wl.num_rows / (ms_per_step * 1e-3),
+        "ms_per_step": ms_per_step,
+        "stages": kernels,
+        "input_side": input_side,
+        "roofline": roofline,
+    }
 
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_b64_ragged")
+    ap.add_argument("--extra-workloads", default="decode_b64_32k",
+                    help="comma-separated workloads also timed and reported under `extra` ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch the timed steps eagerly")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB mebibytes (counter calibration)")
+    args = ap.parse_args()
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the DSA step is not "
+              "sharded across GPUs in this library", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from dsa_workloads import CONFIGS
+
+    cfg = CONFIGS[args.workload]
+    wl, m = measure(cfg, args.steps, args.warmup, graph=not args.no_graph)
     result = {
         "metric": METRIC,
-        "value": tokens_per_s,
+        "value": m["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -295,14 +400,30 @@ def main():
                    "ctx_total": int(wl.seq_lens_k.sum()), "ctx_max": wl.max_seq_len_k, "topk": cfg.topk,
                    "page_size": cfg.page_size, "indexer": f"{cfg.idx_heads}x{cfg.idx_dim} {cfg.idx_kind}",
                    "mla": f"{cfg.mla_heads} heads x {cfg.d_latent}+{cfg.d_rope} {cfg.mla_kind}"},
-        "sparse_attn_hbm_gbps": kernels["sparse_mla"]["hbm_gbps"],
-        "stages": kernels,
-        "input_side": input_side,
-        "roofline": roofline,
+        "sparse_attn_hbm_gbps": m["stages"]["sparse_mla"]["hbm_gbps"],
+        "stages": m["stages"],
+        "input_side": m["input_side"],
+        "roofline": m["roofline"],
     }
+    extra = {}
+    for name in [x for x in args.extra_workloads.split(",") if x and x != cfg.name]:
+        del wl
+        torch.cuda.empty_cache()
+        wl_x, mx = measure(CONFIGS[name], args.steps, args.warmup, graph=not args.no_graph,
+                           with_input_side=False)
+        extra[name] = {"tokens_per_s": mx["tokens_per_s"], "ms_per_step": mx["ms_per_step"],
+                       "description": CONFIGS[name].note, "ctx_total": int(wl_x.seq_lens_k.sum()),
+                       "sparse_attn_hbm_gbps": mx["stages"]["sparse_mla"]["hbm_gbps"],
+                       "stages": {k: {kk: v[kk] for kk in ("us", "bound", "hbm_frac", "mfma_frac") if kk in v}
+                                  for k, v in mx["stages"].items()},
+                       "roofline": mx["roofline"]}
+        wl = wl_x
+    if extra:
+        result["extra"] = extra
     if not args.no_cpu_baseline:
+        from dsa_workloads import generate
         print("[bench] timing the oracle on a sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(wl, budget_s=args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(generate(cfg), budget_s=args.cpu_budget)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result))

@@ -34,8 +34,13 @@ Parity status per function (what pins it; see tests/test_oracle_*.py):
 * dsa.indexer_logits ..................... pinned (hand-worked golden example,
   brute-force loops, textbook matmul special case, page-permutation and
   zero-weight-head invariances).
-* dsa.mask_init_and_local ................ pinned (brute force over small
-  rows, the forced positions always selected, the rest ranked as before).
+* dsa.mask_init_and_local ................ pinned (hand-worked golden example
+  of the SGLang page's init/local windows over decode and prefill rows, which
+  rejects an off-by-one local window and a window anchored at the request's
+  length; forced positions always selected, the rest ranked as before).
+* dsa.page_of (absent pages) ............. pinned (the indexer hand example with
+  a page id outside the pool: -inf there, the hand-worked values elsewhere;
+  the attention hand example reduced to its one-index closed form).
 * dsa.topk ............................... pinned (brute-force full sort,
   short-row rule, order-statistic property, affine invariance).
 * dsa.sparse_mla ......................... pinned (closed forms for one index
@@ -63,6 +68,7 @@ from .dsa import (  # noqa: F401
     indexer_logits_row,
     lse_merge,
     mask_init_and_local,
+    page_of,
     row_layout,
     sparse_mla,
     sparse_mla_row,

@@ -69,14 +69,39 @@ def _decode_keys(raw, kind):
     raise ValueError(f"unknown key kind {kind!r}")
 
 
+def page_of(block_table_row, p, page_size, num_pages):
+    """Physical page of logical position `p`, or None when the position names
+    no page of the pool.
+
+    The pages always hand the kernels well-formed tables. The library states
+    what happens otherwise, and the oracle follows it: a table entry outside
+    [0, num_pages) is an absent page. The indexer then scores the position
+    -inf and attention skips it. (A position past the table row's width has
+    no entry at all; callers keep seq_lens_k within the table, and the oracle
+    only guards against indexing past the row.)
+    """
+    slot = int(p) // page_size
+    if slot >= len(block_table_row):
+        return None
+    page = int(block_table_row[slot])
+    if page < 0 or page >= num_pages:
+        return None
+    return page
+
+
 def gather_index_keys(index_cache, block_table_row, n, page_size, head_dim, kind):
     """Keys k[p] (float64 [n, D]) and scales sigma[p] (float64 [n]) of
-    positions 0..n-1 of one request, walked through its block-table row."""
+    positions 0..n-1 of one request, walked through its block-table row.
+    A position on an absent page (`page_of`) gets NaN for its key and scale."""
     elem = 1 if kind == "fp8" else 4
     keys = np.empty((n, head_dim), dtype=np.float64)
     sigma = np.empty(n, dtype=np.float64)
     for p in range(n):
-        page = int(block_table_row[p // page_size])
+        page = page_of(block_table_row, p, page_size, len(index_cache))
+        if page is None:
+            keys[p] = np.nan
+            sigma[p] = np.nan
+            continue
         slot = p % page_size
         record = index_cache[page]
         k_raw = record[slot * head_dim * elem:(slot + 1) * head_dim * elem]
@@ -103,10 +128,18 @@ def indexer_logits_row(q_row, w_row, keys, sigma):
 def mask_init_and_local(logits_row, visible, num_init, num_local):
     """Force the first `num_init` and the last `num_local` visible positions
     into the selection by giving them +inf (SGLang indexer page,
-    `Indexer._mask_init_and_local_tokens`: +inf is scattered at
-    `row_start + arange(num_init)` and at `length - 1 - arange(num_local)`,
-    clamped to the row). Rows start at position 0 here; positions at or past
-    the visible length are not defined anyway. Returns a new array."""
+    `Indexer._mask_init_and_local_tokens`).
+
+    On the page a row's keys start at column `row_start` of the logits. The
+    init columns are `row_start + i` for i < num_init, clamped to the last
+    column; the local columns are `row_start + length - 1 - i` for
+    i < num_local, clamped at column 0. Here every row starts at position 0
+    and `visible` is the row's own length (for a prefill row, the keys that
+    row may see, not the request's). Columns that land outside
+    [0, visible) after those clamps belong to no key of the row, and top-k
+    never reads them. So the forced set is [0, min(num_init, visible)) and
+    [max(visible - num_local, 0), visible). Returns a new array.
+    """
     out = np.array(logits_row, dtype=np.float64, copy=True)
     n = int(visible)
     for i in range(int(num_init)):
@@ -137,6 +170,9 @@ def indexer_logits(q, w, index_cache, block_table, seq_lens_k, cu_seqlens_q,
         longest[info[t].seq] = max(longest.get(info[t].seq, 0), info[t].visible)
     gathered = {b: gather_index_keys(index_cache, block_table[b], n, page_size, head_dim, kind)
                 for b, n in longest.items()}
+    absent = {b: np.array([page_of(block_table[b], p, page_size, len(index_cache)) is None
+                           for p in range(n)], dtype=bool)
+              for b, n in longest.items()}
     out = {}
     for t in wanted:
         r = info[t]
@@ -144,6 +180,7 @@ def indexer_logits(q, w, index_cache, block_table, seq_lens_k, cu_seqlens_q,
         q_row = decode_e4m3fn(q[t]) if kind == "fp8" else np.asarray(q[t], dtype=np.float64)
         w_row = np.asarray(w[t], dtype=np.float64)
         out[t] = indexer_logits_row(q_row, w_row, keys[:r.visible], sigma[:r.visible])
+        out[t][absent[r.seq][:r.visible]] = -np.inf     # absent page: no key to score
         if num_init or num_local:
             out[t] = mask_init_and_local(out[t], r.visible, num_init, num_local)
     return out
@@ -158,9 +195,11 @@ def topk_row(logits_row, visible, k):
       `topk(min(topk, seq_len))` then padding with -1).
     * otherwise the k positions with the largest logits. Ties at the k-th
       value go to the lower position (the pages are silent on ties).
-    The pages leave the order of the selected set to the backend
-    (`topk_transform` "may not be the topk indices" in order); the oracle
-    stores it ascending so sets compare directly.
+    The pages treat the result as a set: the SGLang indexer page lets each
+    attention backend rewrite the top-k output in `topk_transform`, so no
+    order is part of the method. The oracle stores the set in ascending
+    position order, a canonical form in which two equal sets are equal
+    arrays.
     """
     out = np.full(k, -1, dtype=np.int64)
     if visible <= k:
@@ -201,11 +240,16 @@ def gather_latent_rows(latent_cache, block_table_row, positions, page_size, kind
     return np.stack(rows)
 
 
-def _valid_positions(idx_row, seq_len):
-    """Entries that name a token of the request; -1 (and anything outside
-    [0, seq_len)) is skipped, as the pages pad unused top-k slots with -1."""
-    idx_row = np.asarray(idx_row)
-    return idx_row[(idx_row >= 0) & (idx_row < seq_len)]
+def _valid_positions(idx_row, seq_len, block_table_row, page_size, num_pages):
+    """Entries that name a token of the request, in list order, duplicates
+    kept. -1 (the pages pad unused top-k slots with it) and anything outside
+    [0, seq_len) are skipped, and so is a position on an absent page
+    (`page_of`)."""
+    keep = []
+    for p in np.asarray(idx_row).tolist():
+        if 0 <= p < seq_len and page_of(block_table_row, p, page_size, num_pages) is not None:
+            keep.append(p)
+    return np.asarray(keep, dtype=np.int64)
 
 
 def sparse_mla_row(q_row, rows_c, d_latent, scale, return_probs=False):
@@ -252,7 +296,8 @@ def sparse_mla(q, latent_cache, topk_idx, block_table, seq_lens_k, cu_seqlens_q,
     res = {}
     for t in wanted:
         b = info[t].seq
-        pos = _valid_positions(topk_idx[t], int(seq_lens_k[b]))
+        pos = _valid_positions(topk_idx[t], int(seq_lens_k[b]), block_table[b], page_size,
+                               len(latent_cache))
         rows_c = gather_latent_rows(latent_cache, block_table[b], pos, page_size, kind)
         q_row = _decode_latent(q[t], kind)
         if kind == "fp8":

@@ -5,7 +5,9 @@ Tolerances (stated once, used by every parity test):
 * indexer logits: |L_gpu - L_orc| <= 1e-3 * max(|L_orc|, A), where
   A = sum_h |w_h| relu(sigma (q_h . k)) is the magnitude of the terms being
   summed (the relative 1e-3 of the logits, measured against the sum's own
-  scale because signed head weights can cancel toward 0).
+  scale because signed head weights can cancel toward 0). Infinite oracle
+  values (-inf on absent pages, +inf at forced positions) must be matched
+  exactly.
 * top-k on identical logits: bit-exact (same positions, same order).
 * top-k end to end (GPU logits vs oracle logits): the GPU row holds exactly
   min(k, visible) distinct positions in [0, visible) in ascending order, then
@@ -39,8 +41,17 @@ def check_logits(gpu_logits, wl, rows, ref=None):
     for t in rows:
         n = len(ref[t])
         got = np.asarray(gpu_logits[t][:n], dtype=np.float64)
-        bound = LOGIT_RTOL * np.maximum(np.abs(ref[t]), scale[t])
-        err = np.abs(got - ref[t])
+        # an infinite oracle value (a position on an absent page, -inf; a
+        # forced position, +inf) must come out as exactly that value
+        inf = ~np.isfinite(ref[t])
+        if not np.array_equal(got[inf], ref[t][inf]):
+            i = int(np.nonzero(inf & (got != ref[t]))[0][0])
+            raise AssertionError(f"row {t}: position {i} should be {ref[t][i]!r}, gpu {got[i]!r}")
+        fin = ~inf
+        bound = np.zeros(n)
+        bound[fin] = LOGIT_RTOL * np.maximum(np.abs(ref[t][fin]), scale[t][fin])
+        err = np.zeros(n)
+        err[fin] = np.abs(got[fin] - ref[t][fin])
         bad = ~(err <= bound)
         if bad.any():
             i = int(np.argmax(bad))

@@ -92,11 +92,33 @@ def test_full_single_decode_8k():
 
 
 def test_full_ragged_batch64_sampled():
+    """Logits and attention on sampled rows; top-k bit-exact on the GPU's own
+    logits for all 64 rows (the oracle's selection is cheap)."""
     cfg = CONFIGS["decode_b64_ragged"]
     wl = generate(cfg, with_mla=False)
     lens = wl.seq_lens_k
     rows = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 17})
-    _full_check(cfg, rows=rows)
+    wl, _, h = _full_check(cfg, rows=rows)
+    parity.check_topk_exact(h["topk"], h["logits"], parity.visible_of(wl), cfg.topk, range(wl.num_rows))
+
+
+def test_full_all_32k_batch64_sampled():
+    """The literal "ctx 32k" batch: 64 rows of 32,768 keys each."""
+    cfg = CONFIGS["decode_b64_32k"]
+    wl, _, h = _full_check(cfg, rows=[0, 31, 63])
+    parity.check_topk_exact(h["topk"], h["logits"], parity.visible_of(wl), cfg.topk, range(wl.num_rows))
+
+
+def test_full_multi_token_decode_x4_sampled():
+    """next_n = 4 over the ragged batch: the four rows of the shortest and the
+    longest request, and one more."""
+    cfg = CONFIGS["mtp_b64x4_ragged"]
+    wl = generate(cfg, with_mla=False)
+    lens = wl.seq_lens_k
+    b_min, b_max = int(np.argmin(lens)), int(np.argmax(lens))
+    rows = sorted({*range(4 * b_min, 4 * b_min + 4), *range(4 * b_max, 4 * b_max + 4), 101})
+    wl, _, h = _full_check(cfg, rows=rows)
+    parity.check_topk_exact(h["topk"], h["logits"], parity.visible_of(wl), cfg.topk, range(wl.num_rows))
 
 
 def test_full_long_context_128k_sampled():
@@ -132,10 +154,12 @@ def test_full_prefill_sampled():
     _full_check(CONFIGS["prefill_4k_on_16k"], rows=[0, 1, 2047, 4094, 4095])
 
 
-def _shared_pool_indexer(seed, lens, q_lens=None, pool=320, check_rows=()):
+def _shared_pool_indexer(seed, lens, q_lens=None, pool=320, check_rows=(), absent=False):
     """The fp8 indexer on rows whose block tables name pages of one shared pool
     (as shared prefixes do), so that large batches need little memory; the
-    listed rows (and the first, last and longest) against the oracle."""
+    listed rows (and the first, last and longest) against the oracle. With
+    `absent`, one block-table entry in five names no page of the pool (-1 or
+    an id at or past the pool size): those positions must score -inf."""
     _need_gpu()
     import types
     import sparse_mla_attention_dsa_amd as dsa
@@ -148,6 +172,9 @@ def _shared_pool_indexer(seed, lens, q_lens=None, pool=320, check_rows=()):
     T = B if cu is None else int(cu[-1])
     max_len = int(lens.max())
     bt = rng.integers(0, pool, size=(B, -(-max_len // P))).astype(np.int32)
+    if absent:
+        holes = rng.random(bt.shape) < 0.2
+        bt[holes] = rng.choice(np.array([-1, pool, pool + 77], dtype=np.int32), size=int(holes.sum()))
     keys = rng.standard_normal((pool * P, D)).astype(np.float32)
     sig = (np.abs(keys).max(axis=1) / 448.0).astype(np.float32)
     codes = _to_e4m3fn_bytes(keys / sig[:, None])
@@ -187,6 +214,12 @@ def test_indexer_more_rows_than_stream_units():
     _shared_pool_indexer(621, lens, check_rows=(7, 1024, 1025))
 
 
+def test_indexer_general_kernel_absent_pages():
+    """The general fp8 kernel (1,100 decode rows) on block tables with absent pages."""
+    lens = np.random.default_rng(623).integers(1, 3001, size=1100)
+    _shared_pool_indexer(623, lens, check_rows=(3, 1024, 1099), absent=True)
+
+
 def test_indexer_more_requests_than_prefill_blocks():
     """1,030 two-row requests (more than the two-row stream kernel's 512 and
     the prefill kernel's 1,024 requests): the general fp8 kernel with causal
@@ -208,9 +241,6 @@ def test_empty_batch_launches_nothing():
     dsa.dsa_topk(batch, logits, 16, idx)
     torch.cuda.synchronize()
 
-
-if __name__ == "__main__":
-    sys.exit(pytest.main([__file__, "-v"]))
 
 
 @pytest.mark.parametrize("cfg,n_init,n_local", [
@@ -253,3 +283,7 @@ def test_init_and_local_forcing(cfg, n_init, n_local):
             assert forced <= chosen, f"row {t}: a forced position was not selected"
         else:
             assert chosen == set(sorted(forced)[:cfg.topk])
+
+
+if __name__ == "__main__":
+    sys.exit(pytest.main([__file__, "-v"]))

@@ -82,3 +82,19 @@ def test_many_rows_single_phase():
     rng = np.random.default_rng(17)
     lengths = [int(x) for x in rng.integers(1, 6000, size=300)]
     assert _run(lengths, 512, _ties, seed=18) == 0   # enough rows: one work-group per row
+
+
+def test_many_long_rows_uncached():
+    """300 tie-heavy rows of 33k-70k positions: enough rows for one work-group
+    per row, and too long for the LDS key cache, so every pass re-reads the
+    row (the uncached selection and its variable-length output runs)."""
+    rng = np.random.default_rng(19)
+    lengths = [int(x) for x in rng.integers(33000, 70001, size=300)]
+    assert _run(lengths, 2048, _ties, seed=20) == 0
+
+
+def test_merge_of_more_candidates_than_the_cache():
+    """k = 3000 over 340k positions: eleven 32,768-position chunks give 33,000
+    candidates, more than the merge's LDS key cache, so the merge selection
+    runs uncached."""
+    assert _run([340000, 100000, 5000], 3000, _ties, seed=21) > 0

@@ -159,3 +159,18 @@ def test_canaries_are_never_read():
     got = indexer_logits(wl.q_idx, wl.w, wl.index_cache, wl.block_table, wl.seq_lens_k, None, 16, "f32")
     assert len(got[0]) == 100 and len(got[1]) == 33
     assert all(np.isfinite(v).all() for v in got.values())
+
+
+@pytest.mark.parametrize("bad_page", [-1, 2, 1 << 20])
+def test_absent_page_scores_minus_inf(golden_dir, bad_page):
+    """A block-table entry outside [0, num_pages) names no page: its positions
+    score -inf and the others keep the hand-worked values. Logical page 1
+    (positions 2, 3) is made absent; the pool has 2 pages."""
+    ex, q, w, cache, bt = _hand_example(golden_dir)
+    bt_bad = bt.copy()
+    bt_bad[0, 1] = bad_page
+    got = indexer_logits(q, w, cache, bt_bad, np.array([4]), None, 2, "f32")[0]
+    want = np.array(ex["expected_logits"][:2] + [-np.inf, -np.inf])
+    assert np.array_equal(got, want)
+    assert list(oracle.topk_row(got, 4, 3)[:3]) == [0, 1, 2]   # -inf ties go to the lower position
+

@@ -24,6 +24,36 @@ def test_hand_worked_example(golden_dir):
     np.testing.assert_allclose(res[1], np.array(ex["expected_lse"]), rtol=1e-7)
 
 
+@pytest.mark.parametrize("bad_page", [-1, 2, 99])
+def test_hand_example_skips_absent_pages(golden_dir, bad_page):
+    """Entries whose page is outside the pool are skipped like -1: with the
+    hand example's row 0 on an absent page, only row 2 remains, which is the
+    one-index closed form out = C[:Dl], lse = z."""
+    ex = json.load(open(os.path.join(golden_dir, "mla_hand_example.json")))
+    rows = np.array(ex["cache_rows"], dtype=np.float32)
+    bt = np.array([[1, 0]], dtype=np.int32)
+    latent = scatter_tokens(rows, bt[0], 2, 2)
+    q = np.array(ex["q"], dtype=np.float32)[None]
+    bt_bad = np.array([[bad_page, 0]], dtype=np.int32)     # logical page 0 (rows 0, 1) absent
+    idx = np.array([[2, -1, 0, 1, 0]])
+    out, lse = sparse_mla(q, latent, idx, bt_bad, np.array([3]), None, 2, 2, 1.0, "f32")[0]
+    np.testing.assert_allclose(out, [[0.0, 1.0]], rtol=0, atol=0)
+    np.testing.assert_allclose(lse, [np.float32(1.0986122886681098)], rtol=1e-7)
+
+
+def test_hand_example_duplicates_and_order():
+    """Duplicate entries count twice (two copies of row 2 against one of row
+    0: weights 6/7 and 1/7); the order of the entries does not matter."""
+    rows = np.array([[1.0, 0.0, 0.0], [5.0, 5.0, 5.0], [0.0, 1.0, np.log(3.0)]], dtype=np.float64)
+    bt = np.array([[1, 0]], dtype=np.int32)
+    latent = scatter_tokens(rows, bt[0], 2, 2)
+    q = np.array([[[0.0, 0.0, 1.0]]])
+    for order in ([2, 0, 2], [0, 2, 2], [2, 2, 0, -1]):
+        out, lse = sparse_mla(q, latent, np.array([order]), bt, np.array([3]), None, 2, 2, 1.0, "f64")[0]
+        np.testing.assert_allclose(out, [[1.0 / 7.0, 6.0 / 7.0]], rtol=1e-15)
+        np.testing.assert_allclose(lse, [np.log(7.0)], rtol=1e-15)
+
+
 def test_lse_merge_hand_example(golden_dir):
     ex = json.load(open(os.path.join(golden_dir, "lse_merge_hand_example.json")))
     o, l = lse_merge(np.array(ex["o1"]), np.array(ex["lse1"]), np.array(ex["o2"]), np.array(ex["lse2"]))
