@@ -32,9 +32,10 @@
  *   struct itself is read on the host during the call and may be freed after it.
  * - Every call is asynchronous on `stream` (a hipStream_t; 0 = the null
  *   stream), never synchronizes the host, allocates no memory, keeps no state
- *   between calls and is safe to call from several threads. Calls contain no
- *   host-device synchronization and no memset nodes, so they can be captured
- *   into a HIP graph.
+ *   between calls and is safe to call from several threads (except
+ *   sparse_mla_decode_noalloc, which keeps its partials in a static per-GPU
+ *   array: see there). Calls contain no host-device synchronization and no
+ *   memset nodes, so they can be captured into a HIP graph.
  * - The caller owns every buffer. Inputs are read-only; outputs must not alias
  *   inputs.
  * - Arguments are validated on the host before anything is launched. On error
@@ -296,6 +297,32 @@ dsa_status_t sparse_mla_prefill_fp8(const dsa_batch_t *batch,
                                     void *out, float *lse,
                                     void *workspace, size_t workspace_bytes,
                                     dsa_stream_t stream);
+
+/*
+ * sparse_mla_decode_noalloc - sparse_mla_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same attention, arguments and entry
+ * rules as sparse_mla_decode, without the workspace arguments. The split-KV
+ * partials go to a static device array of the library, 32 MiB per GPU, which
+ * each GPU the library runs on holds until the process ends. The call itself
+ * allocates nothing.
+ *
+ * A batch whose partials need more than 32 MiB (dsa_workspace_bytes(
+ * DSA_OP_MLA_DECODE, ...) > 33554432, e.g. k > 2048 over very many rows)
+ * returns DSA_ERR_UNSUPPORTED before anything is launched; use
+ * sparse_mla_decode with a workspace then. Every call on one GPU shares that
+ * GPU's array and leaves its partials in it: calls that may overlap on one GPU
+ * (on different streams, or from several threads without ordering) race and
+ * must be serialized by the caller. The array is looked up for the current
+ * device (hipGetDevice), which must be the device of `stream`.
+ */
+dsa_status_t sparse_mla_decode_noalloc(const dsa_batch_t *batch,
+                                       const void *q, const void *kv_cache, dsa_dtype_t dtype,
+                                       const int32_t *topk_idx, int32_t k,
+                                       int32_t num_heads, int32_t d_latent, int32_t d_rope,
+                                       float softmax_scale,
+                                       void *out, float *lse,
+                                       dsa_stream_t stream);
 
 /*
  * dsa_workspace_bytes - device workspace an op needs for this batch (host-only,

@@ -19,7 +19,7 @@ __all__ = [
     "DSA_OP_MLA_PREFILL", "DsaError", "DsaBatch", "lib", "library_path", "make_batch",
     "dsa_indexer_logits", "dsa_topk", "sparse_mla_decode", "sparse_mla_prefill",
     "dsa_quant_index_q", "dsa_store_index_k", "sparse_mla_decode_fp8", "sparse_mla_prefill_fp8",
-    "dsa_workspace_bytes", "dsa_version", "EXPORTED_SYMBOLS",
+    "sparse_mla_decode_noalloc", "dsa_workspace_bytes", "dsa_version", "EXPORTED_SYMBOLS",
 ]
 
 DSA_OK, DSA_ERR_INVALID_ARGUMENT, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE_TOO_SMALL, DSA_ERR_HIP = range(5)
@@ -29,7 +29,8 @@ DSA_OP_TOPK, DSA_OP_MLA_DECODE, DSA_OP_MLA_PREFILL = range(3)
 EXPORTED_SYMBOLS = (
     "dsa_indexer_logits", "dsa_topk", "sparse_mla_decode", "sparse_mla_prefill",
     "dsa_quant_index_q", "dsa_store_index_k", "sparse_mla_decode_fp8", "sparse_mla_prefill_fp8",
-    "dsa_workspace_bytes", "dsa_status_string", "dsa_last_error", "dsa_version",
+    "sparse_mla_decode_noalloc", "dsa_workspace_bytes", "dsa_status_string", "dsa_last_error",
+    "dsa_version",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -83,6 +84,8 @@ def lib():
         f = getattr(L, name)
         f.argtypes = [P, V, V, I32, V, I32, I32, I32, I32, F32, V, V, V, SZ, V]
         f.restype = I32
+    L.sparse_mla_decode_noalloc.argtypes = [P, V, V, I32, V, I32, I32, I32, I32, F32, V, V, V]
+    L.sparse_mla_decode_noalloc.restype = I32
     for name in ("sparse_mla_decode_fp8", "sparse_mla_prefill_fp8"):
         f = getattr(L, name)
         f.argtypes = [P, V, F32, V, F32, V, I32, I32, I32, I32, F32, V, V, V, SZ, V]
@@ -196,6 +199,18 @@ def sparse_mla_prefill(batch, q, kv_cache, topk_idx, softmax_scale, out, lse=Non
                        *, d_latent=None, stream=None):
     _mla(lib().sparse_mla_prefill, batch, q, kv_cache, topk_idx, softmax_scale, out, lse, workspace,
          d_latent, stream)
+
+
+def sparse_mla_decode_noalloc(batch, q, kv_cache, topk_idx, softmax_scale, out, lse=None, *, d_latent=None,
+                              stream=None):
+    """sparse_mla_decode with its split partials in the library's static
+    per-GPU scratch (no workspace argument, nothing allocated)."""
+    code = _dtype_code(q)
+    Hm, Dqk = int(q.shape[1]), int(q.shape[2])
+    Dl = int(out.shape[2]) if d_latent is None else d_latent
+    _check(lib().sparse_mla_decode_noalloc(batch.ref(), _ptr(q), _ptr(kv_cache), code, _ptr(topk_idx),
+                                           int(topk_idx.shape[1]), Hm, Dl, Dqk - Dl, float(softmax_scale),
+                                           _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def _mla_fp8(fn, batch, q, q_scale, kv_cache, kv_scale, topk_idx, softmax_scale, out, lse, workspace, stream):

@@ -16,7 +16,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
 
-SOURCES = ["dsa_api.cpp", "indexer.hip", "topk.hip", "sparse_mla.hip", "sparse_mla_fp8.hip", "quant.hip"]
+SOURCES = ["dsa_api.cpp", "indexer.hip", "topk.hip", "sparse_mla.hip", "sparse_mla_fp8.hip", "quant.hip",
+           "scratch.hip"]
 
 ARCH = os.environ.get("DSA_OFFLOAD_ARCH", "gfx950")
 

@@ -189,6 +189,16 @@ dsa_status_t run_mla(const dsa_batch_t* batch, bool decode, const void* q, const
 
 }  // namespace
 
+dsa_status_t dsa::set_error(dsa_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
 extern "C" {
 
 dsa_status_t dsa_indexer_logits(const dsa_batch_t* batch, const void* q, dsa_dtype_t q_dtype,

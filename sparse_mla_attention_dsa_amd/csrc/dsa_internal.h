@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "dsa.h"
+
 namespace dsa {
 
 struct BatchView {
@@ -122,5 +124,9 @@ hipError_t launch_mla_f32(const MlaParams& p, hipStream_t s);
 hipError_t launch_mla_fp8(const MlaParams& p, hipStream_t s);
 hipError_t launch_mla_combine_bf16(const MlaParams& p, hipStream_t s);
 int mla_fp8_splits(int num_rows, int k, int heads);
+
+// Records a printf-style message as this thread's dsa_last_error() text and
+// returns `st`.
+dsa_status_t set_error(dsa_status_t st, const char* fmt, ...);
 
 }  // namespace dsa

@@ -259,3 +259,22 @@ def test_fp8_attention_entry_points_validate_on_the_host(L):
     # the plain entry point does not take an fp8 cache (it has no scales)
     assert L.sparse_mla_decode(ctypes.byref(b), V(0x10), V(0x20), dsa.DSA_FP8_E4M3, V(0x30), 2048, 128, 512, 64,
                                0.07, V(0x40), None, V(0x1000), need, None) == dsa.DSA_ERR_UNSUPPORTED
+
+
+def test_noalloc_rejects_partials_beyond_the_scratch(L):
+    """1,024 rows at k = 4096 need two splits each: 1024 x 2 x 128 heads x
+    (512 bf16 + fp32 lse) bytes of partials, far above the 32 MiB scratch. The
+    call is rejected on the host before any device work."""
+    bt = FakeTensor((1024, 64), ptr=0x10000)
+    sl = FakeTensor((1024,), ptr=0x20000)
+    batch = dsa.make_batch(bt, sl, page_size=64, num_pages=100, max_seq_len_k=4096, max_seq_len_q=1)
+    need = dsa.dsa_workspace_bytes(dsa.DSA_OP_MLA_DECODE, batch, 4096, 128, 512, dsa.DSA_BF16)
+    assert need > 32 << 20
+    q = FakeTensor((1024, 128, 576), ptr=0x30000)
+    idx = FakeTensor((1024, 4096), ptr=0x40000)
+    out = FakeTensor((1024, 128, 512), ptr=0x50000)
+    st = L.sparse_mla_decode_noalloc(batch.ref(), ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(0x60000),
+                                     dsa.DSA_BF16, ctypes.c_void_p(idx.data_ptr()), 4096, 128, 512, 64,
+                                     ctypes.c_float(0.07), ctypes.c_void_p(out.data_ptr()), None, None)
+    assert st == dsa.DSA_ERR_UNSUPPORTED
+    assert b"static scratch" in L.dsa_last_error()
