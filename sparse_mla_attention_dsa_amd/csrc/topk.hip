@@ -44,6 +44,7 @@ constexpr int kTkCand = 4032;              // keys sharing the top 12 bits kept 
 constexpr int kTkRun = kTkCache / kTkThreads;   // 32 positions per thread in the output pass (cached rows)
 constexpr int kTkCandPerWave = kTkCand / kTkWaves; // 252 candidate slots per wave
 static_assert(kTkRun == 32, "the output pass handles one 32-position mask per cached run");
+static_assert(kTkCache / (kTkPer * kTkThreads) * kTkPer == 32, "a cached selection gives each thread at most 32 positions");
 
 struct TopkShared {
   uint32_t hist[kTkBins];
@@ -250,7 +251,41 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
   // slots makes the last digit take the full pass instead.
   const int wave = wave_id();
   uint32_t wcnt = 0;                                   // this wave's matches so far (wave-uniform)
-  for (int i = kTkPer * tid; i < n; i += kTkPer * kTkThreads) {
+  // one matching key of the lane per round: histogram count and list append
+  auto take_match = [&](bool m, uint32_t x) {
+    if (m) atomicAdd(&sh.hist[(x >> 8) & 0xfffu], 1u);
+    const uint64_t mask = __ballot(m);
+    const uint32_t slot = wcnt + lanes_below(mask);
+    if (keep && m && slot < (uint32_t)kTkCandPerWave) sh.cand[wave * kTkCandPerWave + slot] = x;
+    wcnt += (uint32_t)__builtin_popcountll(mask);
+  };
+  if (cached) {
+    // The thread's (at most 32) positions i = 8 tid + 8192 j + e first give
+    // one match mask; the matches are then handled in rounds of one per lane,
+    // so the rounds of the whole pass number the most matches of one lane.
+    uint32_t mm = 0;
+#pragma unroll
+    for (int j = 0; j < kTkCache / (kTkPer * kTkThreads); ++j) {
+      const int i = kTkPer * tid + kTkPer * kTkThreads * j;
+      if (i < n) {
+        uint32_t u[kTkPer];
+        load8<kKeys>(src, sh, true, n, i, u);
+#pragma unroll
+        for (int e = 0; e < kTkPer; ++e) mm |= ((i + e < n && (u[e] >> 20) == prefix) ? 1u : 0u) << (kTkPer * j + e);
+      }
+    }
+    while (__ballot(mm != 0u)) {
+      const bool m = mm != 0u;
+      uint32_t x = 0;
+      if (m) {
+        const int b = __builtin_ctz(mm);
+        mm &= mm - 1u;
+        x = sh.keys[kslot(kTkPer * tid + kTkPer * kTkThreads * (b / kTkPer) + b % kTkPer)];
+      }
+      take_match(m, x);
+    }
+  }
+  for (int i = kTkPer * tid; !cached && i < n; i += kTkPer * kTkThreads) {
     uint32_t u[kTkPer];
     load8<kKeys>(src, sh, cached, n, i, u);
     // matches are rare: each round handles one match per lane, so a wave issues
@@ -267,12 +302,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
         x = u[0];
 #pragma unroll
         for (int q = 1; q < kTkPer; ++q) x = (e == q) ? u[q] : x;
-        atomicAdd(&sh.hist[(x >> 8) & 0xfffu], 1u);
       }
-      const uint64_t mask = __ballot(m);
-      const uint32_t slot = wcnt + lanes_below(mask);
-      if (keep && m && slot < (uint32_t)kTkCandPerWave) sh.cand[wave * kTkCandPerWave + slot] = x;
-      wcnt += (uint32_t)__builtin_popcountll(mask);
+      take_match(m, x);
     }
   }
   if (lane_id() == 0) sh.wave_cand[wave] = wcnt;
@@ -354,11 +385,20 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
     cgt += (uint32_t)__builtin_popcount(gtm);
     ceq += (uint32_t)__builtin_popcount(eqm);
   }
-  uint32_t total_gt, total_eq;
-  const uint32_t gt_incl = block_scan(sh, cgt, 1, &total_gt);
-  const uint32_t eq_incl = block_scan(sh, ceq, 0, &total_eq);
-  uint32_t eq_before = eq_incl - ceq;
-  uint32_t slot = (gt_incl - cgt) + (eq_before < need ? eq_before : need);
+  // winners and ties before this thread's run: for selections below 65536
+  // elements one scan of both counts, (> thr) in the high half and (== thr)
+  // in the low half (neither reaches 2^16, so no carry crosses); else two
+  uint32_t gt_before, eq_before, total;
+  if (n < 65536) {
+    const uint32_t both = (cgt << 16) | ceq;
+    const uint32_t before = block_scan(sh, both, 0, &total) - both;
+    gt_before = before >> 16;
+    eq_before = before & 0xffffu;
+  } else {
+    gt_before = block_scan(sh, cgt, 1, &total) - cgt;
+    eq_before = block_scan(sh, ceq, 0, &total) - ceq;
+  }
+  uint32_t slot = gt_before + (eq_before < need ? eq_before : need);
   if (cgt + ceq) {
     for (int p0 = run0; p0 < run0 + run_len && p0 < n; p0 += 32) {
       uint32_t gtm = gtm0, eqm = eqm0;
