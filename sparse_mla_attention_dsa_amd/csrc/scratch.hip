@@ -38,7 +38,9 @@ extern "C" dsa_status_t sparse_mla_decode_noalloc(const dsa_batch_t* batch, cons
                                                   int32_t d_latent, int32_t d_rope, float softmax_scale,
                                                   void* out, float* lse, dsa_stream_t stream) {
   const size_t need = dsa_workspace_bytes(DSA_OP_MLA_DECODE, batch, k, num_heads, d_latent, dtype);
-  if (need == (size_t)-1) return DSA_ERR_INVALID_ARGUMENT;       // dsa_last_error() says why
+  if (need == (size_t)-1)   // invalid or unsupported: the plain call reports which, before any launch
+    return sparse_mla_decode(batch, q, kv_cache, dtype, topk_idx, k, num_heads, d_latent, d_rope, softmax_scale,
+                             out, lse, nullptr, 0, stream);
   if (need > kScratchBytes)
     return dsa::set_error(DSA_ERR_UNSUPPORTED,
                           "sparse_mla_decode_noalloc: the split partials of this batch need %zu bytes, more "

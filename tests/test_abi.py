@@ -278,3 +278,17 @@ def test_noalloc_rejects_partials_beyond_the_scratch(L):
                                      ctypes.c_float(0.07), ctypes.c_void_p(out.data_ptr()), None, None)
     assert st == dsa.DSA_ERR_UNSUPPORTED
     assert b"static scratch" in L.dsa_last_error()
+
+
+def test_noalloc_reports_the_plain_calls_status(L):
+    """An unsupported head count gives the same status as sparse_mla_decode (no launch)."""
+    bt = FakeTensor((4, 8), ptr=0x10000)
+    sl = FakeTensor((4,), ptr=0x20000)
+    batch = dsa.make_batch(bt, sl, page_size=64, num_pages=100, max_seq_len_k=512, max_seq_len_q=1)
+    V = ctypes.c_void_p
+    args = (batch.ref(), V(0x30000), V(0x60000), dsa.DSA_BF16, V(0x40000), 2048, 96, 512, 64, ctypes.c_float(0.07),
+            V(0x50000), None)
+    assert L.sparse_mla_decode_noalloc(*args, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert L.sparse_mla_decode(*args, V(0x1000), 1 << 20, None) == dsa.DSA_ERR_UNSUPPORTED
+    bad = args[:5] + (0,) + args[6:]                      # k = 0
+    assert L.sparse_mla_decode_noalloc(*bad, None) == dsa.DSA_ERR_INVALID_ARGUMENT
