@@ -64,6 +64,7 @@ def algorithmic_work(wl):
       each row reads its q and gates and writes 4 B per visible logit;
       2 H D FLOP per (row, visible key).
     * top-k: each row reads its visible logits (4 B each) and writes k indices.
+    * indexer + top-k fused: the indexer's reads and the top-k's writes.
     * sparse MLA: each selected row is gathered once per query row that
       selects it (1,152 B for bf16 576-wide rows); decode rows of different
       requests share nothing, so this is HBM traffic. Rows of one request
@@ -85,6 +86,7 @@ def algorithmic_work(wl):
                  + T * (H * D * esize + 4 * H))
     idx_flops = int(vis.sum()) * 2 * H * D
     topk_bytes = int(vis.sum()) * 4 + T * 4 * k
+    fused_bytes = idx_bytes - int(vis.sum()) * 4 + T * 4 * k
     sel = np.minimum(vis, k)
     Hm, Dl, Dr = cfg.mla_heads, cfg.d_latent, cfg.d_rope
     msize = {"bf16": 2, "fp8": 1}.get(cfg.mla_kind, 4)          # cached row and query element
@@ -111,6 +113,13 @@ def algorithmic_work(wl):
                     "units": int(vis.sum())},
         "topk": {"bytes": topk_bytes, "flops": 0, "peak_tflops": None, "bound": "hbm",
                  "per_unit": f"4 B per visible score (+{4 * k} B per row)", "units": int(vis.sum())},
+        # the fused call reads the keys, q and gates and writes the lists: no logits
+        "indexer_topk": {"bytes": fused_bytes, "flops": idx_flops, "peak_tflops": idx_peak,
+                         "bound": _bound(idx_flops, fused_bytes, idx_peak),
+                         "per_unit": f"{key_bytes} B per key of a request (read once for its rows) + "
+                                     f"{H * D * esize + 4 * H + 4 * k} B per row; {2 * H * D} FLOP per "
+                                     f"(row, visible key)",
+                         "units": int(vis.sum())},
         "sparse_mla": {"bytes": mla_bytes, "flops": mla_flops, "peak_tflops": mla_peak,
                        "bound": _bound(mla_flops, mla_bytes, mla_peak),
                        "gather_bytes": gathered + T * per_row_io,
@@ -230,7 +239,7 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n}))
 
 
-def measure(cfg, K, W, graph=True, with_input_side=True):
+def measure(cfg, K, W, graph=True, with_input_side=True, fused=False):
     """Generate `cfg`, run W eager warm-up steps, time K steps, time the stages.
 
     The K timed steps are one HIP graph (captured once, replayed once), as a
@@ -248,7 +257,7 @@ def measure(cfg, K, W, graph=True, with_input_side=True):
     t_gen = time.perf_counter()
     wl = generate(cfg)
     print(f"[bench] generated {cfg.name} in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
-    step = make_step(wl, device="cuda:0")
+    step = make_step(wl, device="cuda:0", fused=fused)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
@@ -257,7 +266,10 @@ def measure(cfg, K, W, graph=True, with_input_side=True):
     torch.cuda.synchronize()
     print(f"[bench] {cfg.name}: warmup done ({W} steps)", file=sys.stderr, flush=True)
 
-    stages = (("indexer", step.indexer), ("topk", step.select), ("sparse_mla", step.attend))
+    if fused:
+        stages = (("indexer_topk", step.index_select), ("sparse_mla", step.attend))
+    else:
+        stages = (("indexer", step.indexer), ("topk", step.select), ("sparse_mla", step.attend))
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     if not graph:
         run_all = lambda: [step.run() for _ in range(K)]
@@ -286,7 +298,7 @@ def measure(cfg, K, W, graph=True, with_input_side=True):
         torch.cuda._sleep(40_000_000)                        # ~20 ms of GPU spin
     except Exception:
         pass
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(K)]
     for i in range(K):
         ev[i][0].record(stream)
         for j, (_, fn) in enumerate(stages):
@@ -301,7 +313,8 @@ def measure(cfg, K, W, graph=True, with_input_side=True):
 
     work = algorithmic_work(wl)
     kernels = {}
-    for name, w in work.items():
+    for name in stage_ms:
+        w = work[name]
         t_s = stage_ms[name] * 1e-3
         gbps = w["bytes"] / t_s / 1e9
         kernels[name] = {
@@ -358,6 +371,8 @@ def main():
                     help="comma-separated workloads also timed and reported under `extra` ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch the timed steps eagerly")
+    ap.add_argument("--fused", action="store_true",
+                    help="indexer and top-k as one call (dsa_indexer_topk, no logits in memory)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB mebibytes (counter calibration)")
@@ -377,7 +392,7 @@ def main():
     from dsa_workloads import CONFIGS
 
     cfg = CONFIGS[args.workload]
-    wl, m = measure(cfg, args.steps, args.warmup, graph=not args.no_graph)
+    wl, m = measure(cfg, args.steps, args.warmup, graph=not args.no_graph, fused=args.fused)
     result = {
         "metric": METRIC,
         "value": m["tokens_per_s"],
@@ -396,6 +411,8 @@ def main():
                          "converted exactly), fp32 accumulate and softmax"),
         "data": "synthetic",
         "launch": "eager" if args.no_graph else "hip graph of the timed steps",
+        "selection": ("dsa_indexer_topk (fused, no logits in memory)" if args.fused
+                      else "dsa_indexer_logits + dsa_topk"),
         "config": {"workload": cfg.name, "description": cfg.note, "batch": cfg.batch,
                    "ctx_total": int(wl.seq_lens_k.sum()), "ctx_max": wl.max_seq_len_k, "topk": cfg.topk,
                    "page_size": cfg.page_size, "indexer": f"{cfg.idx_heads}x{cfg.idx_dim} {cfg.idx_kind}",
@@ -410,7 +427,7 @@ def main():
         del wl
         torch.cuda.empty_cache()
         wl_x, mx = measure(CONFIGS[name], args.steps, args.warmup, graph=not args.no_graph,
-                           with_input_side=False)
+                           with_input_side=False, fused=args.fused)
         extra[name] = {"tokens_per_s": mx["tokens_per_s"], "ms_per_step": mx["ms_per_step"],
                        "description": CONFIGS[name].note, "ctx_total": int(wl_x.seq_lens_k.sum()),
                        "sparse_attn_hbm_gbps": mx["stages"]["sparse_mla"]["hbm_gbps"],

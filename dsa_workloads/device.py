@@ -24,7 +24,7 @@ def upload(wl, device="cuda"):
     return d
 
 
-def make_step(wl, device="cuda"):
+def make_step(wl, device="cuda", fused=False):
     from sparse_mla_attention_dsa_amd.step import DsaStep
 
     d = upload(wl, device)
@@ -35,4 +35,5 @@ def make_step(wl, device="cuda"):
                    num_rows=wl.num_rows, q_idx=d["q_idx"], w=d["w"], index_cache=d["index_cache"],
                    q_mla=d["q_mla"], kv_cache=d["kv_cache"], topk=cfg.topk,
                    softmax_scale=cfg.softmax_scale, d_latent=cfg.d_latent,
-                   mla_scales=(wl.extras["q_scale"], wl.extras["kv_scale"]) if cfg.mla_kind == "fp8" else None)
+                   mla_scales=(wl.extras["q_scale"], wl.extras["kv_scale"]) if cfg.mla_kind == "fp8" else None,
+                   fused=fused)

@@ -5,6 +5,7 @@
  *
  *   dsa_indexer_logits  lightning-indexer scores over a paged fp8 index-K cache
  *   dsa_topk            per-row top-k of those scores with causal/length masking
+ *   dsa_indexer_topk    both in one call, without the scores in memory
  *   sparse_mla_decode   sparse MLA attention over the selected latent rows
  *   sparse_mla_prefill  (decode: one query row per request; prefill: many)
  *
@@ -87,7 +88,8 @@ typedef enum {
 typedef enum {
   DSA_OP_TOPK = 0,
   DSA_OP_MLA_DECODE = 1,
-  DSA_OP_MLA_PREFILL = 2
+  DSA_OP_MLA_PREFILL = 2,
+  DSA_OP_INDEXER_TOPK = 3
 } dsa_op_t;
 
 typedef struct {
@@ -202,6 +204,36 @@ dsa_status_t dsa_topk(const dsa_batch_t *batch,
                       int32_t *topk_idx,
                       void *workspace, size_t workspace_bytes,
                       dsa_stream_t stream);
+
+/*
+ * dsa_indexer_topk - the lightning-indexer scores and their per-row top-k in
+ * one call, with no [rows x keys] score matrix in memory (SGLang page:
+ * Indexer._get_topk_ragged materialises the scores of a batch, in row chunks
+ * when _should_chunk_mqa_logits finds them too large, and hands them to
+ * topk_transform; this call gives the same top-k lists without them).
+ *
+ * topk_idx[t] is what dsa_topk(k) writes for the scores that
+ * dsa_indexer_logits(FP8_E4M3, num_init_tokens, num_local_tokens) computes
+ * for the same inputs: the fp8 contraction and its summation order are those
+ * of the decode-row scores, so for decode and multi-token decode rows the two
+ * paths give identical lists; init/local forcing and absent pages (-inf) as
+ * there. Rows with visible(t) <= k get 0 .. visible(t) - 1, then -1, without
+ * being scored.
+ *
+ * q, w, index_cache: as dsa_indexer_logits with FP8_E4M3 keys and queries
+ *           (64 heads x 128 only, else DSA_ERR_UNSUPPORTED; 16-byte aligned).
+ * topk_idx: [T, k] int32, 1 <= k <= 4096.
+ * workspace: at least dsa_workspace_bytes(DSA_OP_INDEXER_TOPK, ...) bytes of
+ *           device memory (each row's chunks hand their k best (key, position)
+ *           pairs to a merge: 8 bytes x k per started chunk of up to 8192 keys).
+ */
+dsa_status_t dsa_indexer_topk(const dsa_batch_t *batch,
+                              const void *q, const float *w, const void *index_cache,
+                              int32_t num_heads, int32_t head_dim,
+                              int32_t num_init_tokens, int32_t num_local_tokens,
+                              int32_t k, int32_t *topk_idx,
+                              void *workspace, size_t workspace_bytes,
+                              dsa_stream_t stream);
 
 /*
  * sparse_mla_decode / sparse_mla_prefill - sparse MLA attention over the
@@ -328,7 +360,8 @@ dsa_status_t sparse_mla_decode_noalloc(const dsa_batch_t *batch,
  * dsa_workspace_bytes - device workspace an op needs for this batch (host-only,
  * launches nothing). Returns 0 for an op that needs none, and (size_t)-1 when
  * the arguments are invalid (dsa_last_error() says why). `num_heads` and
- * `d_latent` are the MLA ones; they are ignored for DSA_OP_TOPK. `dtype` is the
+ * `d_latent` are the MLA ones; they are ignored for DSA_OP_TOPK and
+ * DSA_OP_INDEXER_TOPK. `dtype` is the
  * MLA dtype (DSA_FP8_E4M3 for the sparse_mla_*_fp8 calls).
  */
 size_t dsa_workspace_bytes(dsa_op_t op, const dsa_batch_t *batch, int32_t k,

@@ -16,18 +16,18 @@ import os
 
 __all__ = [
     "DSA_OK", "DSA_F32", "DSA_BF16", "DSA_FP8_E4M3", "DSA_OP_TOPK", "DSA_OP_MLA_DECODE",
-    "DSA_OP_MLA_PREFILL", "DsaError", "DsaBatch", "lib", "library_path", "make_batch",
-    "dsa_indexer_logits", "dsa_topk", "sparse_mla_decode", "sparse_mla_prefill",
+    "DSA_OP_MLA_PREFILL", "DSA_OP_INDEXER_TOPK", "DsaError", "DsaBatch", "lib", "library_path", "make_batch",
+    "dsa_indexer_logits", "dsa_topk", "dsa_indexer_topk", "sparse_mla_decode", "sparse_mla_prefill",
     "dsa_quant_index_q", "dsa_store_index_k", "sparse_mla_decode_fp8", "sparse_mla_prefill_fp8",
     "sparse_mla_decode_noalloc", "dsa_workspace_bytes", "dsa_version", "EXPORTED_SYMBOLS",
 ]
 
 DSA_OK, DSA_ERR_INVALID_ARGUMENT, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE_TOO_SMALL, DSA_ERR_HIP = range(5)
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = range(3)
-DSA_OP_TOPK, DSA_OP_MLA_DECODE, DSA_OP_MLA_PREFILL = range(3)
+DSA_OP_TOPK, DSA_OP_MLA_DECODE, DSA_OP_MLA_PREFILL, DSA_OP_INDEXER_TOPK = range(4)
 
 EXPORTED_SYMBOLS = (
-    "dsa_indexer_logits", "dsa_topk", "sparse_mla_decode", "sparse_mla_prefill",
+    "dsa_indexer_logits", "dsa_topk", "dsa_indexer_topk", "sparse_mla_decode", "sparse_mla_prefill",
     "dsa_quant_index_q", "dsa_store_index_k", "sparse_mla_decode_fp8", "sparse_mla_prefill_fp8",
     "sparse_mla_decode_noalloc", "dsa_workspace_bytes", "dsa_status_string", "dsa_last_error",
     "dsa_version",
@@ -80,6 +80,8 @@ def lib():
     L.dsa_indexer_logits.restype = I32
     L.dsa_topk.argtypes = [P, V, I64, I32, V, V, SZ, V]
     L.dsa_topk.restype = I32
+    L.dsa_indexer_topk.argtypes = [P, V, V, V, I32, I32, I32, I32, I32, V, V, SZ, V]
+    L.dsa_indexer_topk.restype = I32
     for name in ("sparse_mla_decode", "sparse_mla_prefill"):
         f = getattr(L, name)
         f.argtypes = [P, V, V, I32, V, I32, I32, I32, I32, F32, V, V, V, SZ, V]
@@ -177,6 +179,17 @@ def dsa_topk(batch, logits, k, topk_idx, workspace=None, stream=None):
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().dsa_topk(batch.ref(), _ptr(logits), int(logits.stride(0)), int(k), _ptr(topk_idx),
                           _ptr(workspace), nbytes, _stream(stream)))
+
+
+def dsa_indexer_topk(batch, q, w, index_cache, k, topk_idx, workspace=None, *, num_init_tokens=0,
+                     num_local_tokens=0, stream=None):
+    """dsa_indexer_logits (fp8, 64 x 128) followed by dsa_topk, without the
+    logits in memory; `workspace` holds dsa_workspace_bytes(DSA_OP_INDEXER_TOPK)."""
+    H, D = int(q.shape[1]), int(q.shape[2])
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().dsa_indexer_topk(batch.ref(), _ptr(q), _ptr(w), _ptr(index_cache), H, D, int(num_init_tokens),
+                                  int(num_local_tokens), int(k), _ptr(topk_idx), _ptr(workspace), nbytes,
+                                  _stream(stream)))
 
 
 def _mla(fn, batch, q, kv_cache, topk_idx, softmax_scale, out, lse, workspace, d_latent, stream):

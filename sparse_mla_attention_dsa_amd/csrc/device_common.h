@@ -85,6 +85,23 @@ __device__ __forceinline__ float sum_over_groups(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Reduce-scatter over the four 16-lane groups: p[u] is this lane's partial
+// of quantity u; lane group g (lanes 16g .. 16g + 15) gets the sum over the
+// four groups of quantity g. The swaps pair rows (0, 1) and (2, 3) first
+// (v_permlane16_swap exchanges the odd rows of its first operand with the
+// even rows of its second), then the halves (v_permlane32_swap: upper half of
+// the first with lower half of the second). Quantity u ends as
+// (p_0[u] + p_1[u]) + (p_2[u] + p_3[u]), the association of sum_over_groups,
+// so both give the same floats.
+__device__ __forceinline__ float sum_scatter_over_groups(float p0, float p1, float p2, float p3) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+  const float s01 = __uint_as_float(a[0]) + __uint_as_float(a[1]);   // rows 0, 2: quantity 0; rows 1, 3: 1
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(p2), __float_as_uint(p3), false, false);
+  const float s23 = __uint_as_float(b[0]) + __uint_as_float(b[1]);   // rows 0, 2: quantity 2; rows 1, 3: 3
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(s01), __float_as_uint(s23), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave, on DPP lane moves (no LDS
 // round trip): shifts of 1, 2, 4, 8 lanes inside each 16-lane row, then the
 // last lane of row 0 / row 2 is added to rows 1 / 3, and the last lane of
@@ -111,6 +128,20 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 __device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(gsrc), "s"(lds_addr) : "memory", "m0");
+}
+
+// fp8 (E4M3) 16x16x128 MFMA with fp32 accumulate. All-zero scale operands
+// select the unscaled form of v_mfma_f32_16x16x128_f8f6f4: the plain fp8
+// product (the same values as unit E8M0 scales), under which the wave can issue
+// independent VALU work far better than under the scaled form.
+__device__ __forceinline__ f32x4 mfma_fp8_16x16x128(const i32x8& a, const i32x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// relu as an integer max with 0 on the float's bits (negative floats are
+// negative integers); no NaN quieting is needed.
+__device__ __forceinline__ float relu_bits(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
 }
 
 template <int N>

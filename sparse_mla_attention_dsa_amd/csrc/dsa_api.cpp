@@ -321,7 +321,55 @@ dsa_status_t dsa_topk(const dsa_batch_t* batch, const float* logits, int64_t log
   const size_t cands = (size_t)bv.num_rows * p.chunks * k;
   p.cand_key = p.chunk > 0 ? static_cast<uint32_t*>(workspace) : nullptr;
   p.cand_pos = p.chunk > 0 ? reinterpret_cast<int32_t*>(static_cast<uint32_t*>(workspace) + cands) : nullptr;
+  p.q8 = nullptr;
+  p.w = nullptr;
+  p.cache = nullptr;
+  p.page_bytes = 0;
+  p.num_init = 0;
+  p.num_local = 0;
   return from_hip(launch_topk(p, reinterpret_cast<hipStream_t>(stream)), "top-k launch");
+}
+
+dsa_status_t dsa_indexer_topk(const dsa_batch_t* batch, const void* q, const float* w, const void* index_cache,
+                              int32_t num_heads, int32_t head_dim, int32_t num_init_tokens,
+                              int32_t num_local_tokens, int32_t k, int32_t* topk_idx, void* workspace,
+                              size_t workspace_bytes, dsa_stream_t stream) {
+  BatchView bv;
+  dsa_status_t st = check_batch(batch, &bv);
+  if (st != DSA_OK) return st;
+  if (num_heads != kIdxHeads || head_dim != kIdxDim)
+    return fail(DSA_ERR_UNSUPPORTED, "dsa_indexer_topk needs 64 fp8 heads x 128 (got %d x %d)", num_heads, head_dim);
+  if (k < 1 || k > kTopkMaxK) return fail(DSA_ERR_INVALID_ARGUMENT, "k %d outside [1, %d]", k, kTopkMaxK);
+  if (num_init_tokens < 0 || num_local_tokens < 0)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "num_init_tokens %d / num_local_tokens %d < 0", num_init_tokens,
+                num_local_tokens);
+  if (bv.num_rows > 0 && (!q || !w || !index_cache || !topk_idx))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "q / w / index_cache / topk_idx is NULL");
+  if (bv.num_rows > 0 && !(aligned16(q) && aligned16(w) && aligned16(index_cache)))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "q, w and index_cache must be 16-byte aligned");
+  const size_t need = indexer_topk_workspace_bytes(bv.num_rows, bv.max_seq_len_k, k);
+  if (workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  if (need > 0 && !workspace) return fail(DSA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (bv.num_rows == 0) return ok();
+  TopkParams p;
+  p.batch = bv;
+  p.logits = nullptr;
+  p.stride = bv.max_seq_len_k > 0 ? bv.max_seq_len_k : 1;   // rows end at their visible length
+  p.k = k;
+  p.topk_idx = topk_idx;
+  p.chunk = indexer_topk_chunk(bv.num_rows, bv.max_seq_len_k, k);
+  p.chunks = (bv.max_seq_len_k + p.chunk - 1) / p.chunk;
+  const size_t cands = (size_t)bv.num_rows * p.chunks * k;
+  p.cand_key = static_cast<uint32_t*>(workspace);
+  p.cand_pos = reinterpret_cast<int32_t*>(static_cast<uint32_t*>(workspace) + cands);
+  p.q8 = static_cast<const uint8_t*>(q);
+  p.w = w;
+  p.cache = static_cast<const uint8_t*>(index_cache);
+  p.page_bytes = (int64_t)bv.page_size * (kIdxDim + 4);
+  p.num_init = num_init_tokens;
+  p.num_local = num_local_tokens;
+  return from_hip(launch_indexer_topk(p, reinterpret_cast<hipStream_t>(stream)), "indexer top-k launch");
 }
 
 dsa_status_t sparse_mla_decode(const dsa_batch_t* batch, const void* q, const void* kv_cache,
@@ -372,6 +420,13 @@ size_t dsa_workspace_bytes(dsa_op_t op, const dsa_batch_t* batch, int32_t k, int
       return (size_t)-1;
     }
     return topk_workspace_bytes(bv.num_rows, bv.max_seq_len_k, k);
+  }
+  if (op == DSA_OP_INDEXER_TOPK) {
+    if (k < 1 || k > kTopkMaxK) {
+      fail(DSA_ERR_INVALID_ARGUMENT, "k %d outside [1, %d]", k, kTopkMaxK);
+      return (size_t)-1;
+    }
+    return indexer_topk_workspace_bytes(bv.num_rows, bv.max_seq_len_k, k);
   }
   if (op == DSA_OP_MLA_DECODE || op == DSA_OP_MLA_PREFILL) {
     MlaPlan plan;

@@ -47,6 +47,14 @@ struct TopkParams {
   int32_t chunks;         // chunks of the longest row
   uint32_t* cand_key;     // order-preserving keys
   int32_t* cand_pos;      // positions
+  // fused with the scores (dsa_indexer_topk): the indexer's fp8 inputs; the
+  // chunk selections then take their keys from the scores they compute
+  const uint8_t* q8;      // [T, 64, 128] E4M3 codes
+  const float* w;         // [T, 64] gates
+  const uint8_t* cache;   // index-K pages
+  int64_t page_bytes;
+  int32_t num_init;       // forced positions (init / local), as in IndexerParams
+  int32_t num_local;
 };
 
 struct MlaParams {
@@ -119,6 +127,13 @@ hipError_t launch_indexer_fp8(const IndexerParams& p, hipStream_t s);
 hipError_t launch_indexer_f32(const IndexerParams& p, hipStream_t s);
 hipError_t launch_indexer_force(const IndexerParams& p, hipStream_t s);
 hipError_t launch_topk(const TopkParams& p, hipStream_t s);
+// Scores and top-k in one pass over the index cache, no logits in memory:
+// per (row, chunk of `chunk` keys) the scores go straight into the
+// selection's LDS key cache and the chunk's top k become candidates; a merge
+// over the candidates gives each row's top k.
+int indexer_topk_chunk(int num_rows, int max_len, int k);
+size_t indexer_topk_workspace_bytes(int num_rows, int max_len, int k);
+hipError_t launch_indexer_topk(const TopkParams& p, hipStream_t s);
 hipError_t launch_mla_bf16(const MlaParams& p, hipStream_t s);
 hipError_t launch_mla_f32(const MlaParams& p, hipStream_t s);
 hipError_t launch_mla_fp8(const MlaParams& p, hipStream_t s);

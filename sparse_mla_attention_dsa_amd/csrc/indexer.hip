@@ -32,20 +32,6 @@ constexpr int kIdxWaves = 4;
 constexpr int kIdxGroupsPerWave = 8;                               // 16 keys each
 constexpr int kIdxChunk = 16 * kIdxGroupsPerWave * kIdxWaves;      // 512 keys per work-group
 
-__device__ __forceinline__ f32x4 mfma_fp8_16x16x128(const i32x8& a, const i32x8& b, const f32x4& c) {
-  // format 0 = fp8 e4m3 for both operands, no block scales: all-zero scale
-  // operands select the unscaled v_mfma_f32_16x16x128_f8f6f4, which computes
-  // the plain fp8 product (the same values as unit E8M0 scales) and lets the
-  // wave issue independent VALU work under it far better than the scaled form.
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-}
-
-// relu as an integer max with 0 on the float's bits (negative floats are
-// negative integers): one VALU op, no NaN quieting as fmaxf needs
-__device__ __forceinline__ float relu_bits(float x) {
-  return __int_as_float(max(__float_as_int(x), 0));
-}
-
 __global__ __launch_bounds__(64 * kIdxWaves) void indexer_fp8_kernel(IndexerParams p) {
   __shared__ i32x8 q_lds[kIdxHeads * kIdxDim / 32];   // the row's q, 8 KB
   const BatchView& bv = p.batch;

@@ -28,34 +28,53 @@
 // last digit. The ordered output gives each thread one contiguous run of
 // positions: count winners in the run, one block-wide scan, place the run's
 // winners in order in LDS, then write the row out with coalesced stores.
+//
+// Fused with the scores (dsa_indexer_topk): phase one runs in work-groups of
+// 256 threads, one per (row, chunk of up to 8192 keys), three per CU. Each
+// computes its chunk's lightning-indexer scores itself (the fp8 MFMA
+// contraction of the decode indexer, same operand layout and summation order,
+// so the scores are the same floats), converts them to keys straight into its
+// LDS key cache while counting the first digit, and selects the chunk's
+// candidates from there; the merge phase is the one above. No score reaches
+// memory.
 #include "device_common.h"
 #include "dsa_internal.h"
 
 namespace dsa {
 namespace {
 
-constexpr int kTkThreads = 1024;
-constexpr int kTkWaves = kTkThreads / kWave;
-constexpr int kTkCache = 32768;
+constexpr int kTkThreads = 1024;           // whole-row, chunk and merge selections
+constexpr int kFuThreads = 256;            // fused scores + chunk selection
+constexpr int kFuAhead = 1;                // fused scores: batches of 64 keys in flight per wave
 constexpr int kTkBins = 4096;
 constexpr int kTkLoadUnroll = 8;           // float4 loads in flight per thread
 constexpr int kTkPer = 8;                  // consecutive positions per thread per pass step
-constexpr int kTkCand = 4032;              // keys sharing the top 12 bits kept for the last level
-constexpr int kTkRun = kTkCache / kTkThreads;   // 32 positions per thread in the output pass (cached rows)
-constexpr int kTkCandPerWave = kTkCand / kTkWaves; // 252 candidate slots per wave
-static_assert(kTkRun == 32, "the output pass handles one 32-position mask per cached run");
-static_assert(kTkCache / (kTkPer * kTkThreads) * kTkPer == 32, "a cached selection gives each thread at most 32 positions");
+constexpr int kTkRun = 32;                 // positions per thread in the output pass (cached selections)
+constexpr int kTkCandPerWave = 252;        // candidate slots per wave for the last level
 
+// LDS of a selection by kThreads threads: the key cache holds 32 positions per
+// thread (one output run each), the candidate list 252 keys per wave.
+template <int kThreads>
 struct TopkShared {
+  static constexpr int kWaves = kThreads / kWave;
+  static constexpr int kCache = kTkRun * kThreads;
+  static constexpr int kCand = kWaves * kTkCandPerWave;
   uint32_t hist[kTkBins];
-  alignas(16) uint32_t keys[kTkCache];
-  uint32_t cand[kTkCand];
+  alignas(16) uint32_t keys[kCache];
+  uint32_t cand[kCand];
   uint32_t n_cand;
-  uint32_t wave_cand[kTkWaves];
-  uint32_t wave_sum[2][kTkWaves];
+  uint32_t wave_cand[kWaves];
+  uint32_t wave_sum[2][kWaves];
   uint32_t sel_bin;
   uint32_t sel_above;
 };
+
+constexpr int kTkCache = TopkShared<kTkThreads>::kCache;   // 32768 keys
+constexpr int kFuCache = TopkShared<kFuThreads>::kCache;   // 8192 keys
+// three fused work-groups fit one CU's 160 KiB of LDS
+static_assert(3 * sizeof(TopkShared<kFuThreads>) <= 160 * 1024, "fused selection LDS");
+// the fused scores keep the page of each 16-key group in the (then unused) candidate list
+static_assert(kFuCache / 16 * sizeof(int) <= sizeof(TopkShared<kFuThreads>::cand), "page list");
 
 // LDS word of position p. Each run of 32 positions (one thread's run in the
 // output pass) keeps its eight 16-byte blocks, block j of run r stored at
@@ -74,8 +93,8 @@ __device__ __forceinline__ uint32_t src_key(const void* __restrict__ src, int q)
 }
 
 // Keys of elements [i, i + 8) (i a multiple of 8); elements >= n give 0.
-template <bool kKeys>
-__device__ __forceinline__ void load8(const void* __restrict__ src, const TopkShared& sh, bool cached,
+template <bool kKeys, int kThreads>
+__device__ __forceinline__ void load8(const void* __restrict__ src, const TopkShared<kThreads>& sh, bool cached,
                                       int n, int i, uint32_t (&u)[kTkPer]) {
   if (cached) {
     const i32x4 a = *reinterpret_cast<const i32x4*>(sh.keys + kslot(i));
@@ -100,14 +119,16 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-__device__ __forceinline__ uint32_t block_scan(TopkShared& sh, uint32_t v, int buf, uint32_t* total) {
+template <int kThreads>
+__device__ __forceinline__ uint32_t block_scan(TopkShared<kThreads>& sh, uint32_t v, int buf, uint32_t* total) {
+  constexpr int kWaves = TopkShared<kThreads>::kWaves;
   const int lane = lane_id(), wave = wave_id();
   const uint32_t incl = wave_inclusive_scan(v);
   if (lane == kWave - 1) sh.wave_sum[buf][wave] = incl;
   __syncthreads();
   uint32_t before = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kTkWaves; ++w) {
+  for (int w = 0; w < kWaves; ++w) {
     const uint32_t s = sh.wave_sum[buf][w];
     before += (w < wave) ? s : 0u;
     tot += s;
@@ -118,10 +139,11 @@ __device__ __forceinline__ uint32_t block_scan(TopkShared& sh, uint32_t v, int b
 
 // Largest bin b whose suffix count sum_{b' >= b} hist[b'] reaches `need`; also
 // the count strictly above it.
-__device__ void select_bin(TopkShared& sh, int nbins, uint32_t need, int buf, uint32_t* bin,
+template <int kThreads>
+__device__ void select_bin(TopkShared<kThreads>& sh, int nbins, uint32_t need, int buf, uint32_t* bin,
                            uint32_t* above) {
   const int tid = threadIdx.x;
-  const int per = nbins >= kTkThreads ? nbins / kTkThreads : 1;
+  const int per = nbins >= kThreads ? nbins / kThreads : 1;
   const int active = nbins / per;
   // thread tid owns bins nbins-1-per*tid down to nbins-per*(tid+1), counted from the top
   uint32_t local = 0;
@@ -148,12 +170,133 @@ __device__ void select_bin(TopkShared& sh, int nbins, uint32_t need, int buf, ui
   *above = sh.sel_above;
 }
 
-enum TopkMode { kWholeRow = 0, kChunk = 1, kMerge = 2 };
+enum TopkMode { kWholeRow = 0, kChunk = 1, kMerge = 2, kFused = 3 };
 
-template <int kMode>
-__global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
+// Fused phase one: the lightning-indexer scores of positions [base, base + n)
+// of row t (request b, visible keys `vis`) into the LDS key cache, with the
+// first-digit histogram. The contraction is the decode indexer's: lane (c, g)
+// of a 16-key group holds bytes [32g, 32g + 32) of head 16m + c of q (A) and
+// of key c (B); the 16 relu'd, gated head values of a lane are summed in
+// order, then over the four lane groups, then scaled by the key's sigma. A
+// wave takes batches of four groups (64 keys), batch j + waves while batch j
+// is computed, and after a batch lane (c, g) owns key c of group g. Positions
+// on absent pages get -inf, forced (init / local) positions +inf.
+template <int kThreads>
+__device__ __forceinline__ void fused_scores(const TopkParams& p, TopkShared<kThreads>& sh, int t, int b,
+                                             int base, int n, int vis) {
+  constexpr int kWaves = TopkShared<kThreads>::kWaves;
+  const BatchView& bv = p.batch;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(wave_id());
+  const int g = lane >> 4, c = lane & 15;
+  const int P = bv.page_size;
+  const int ngroups = (n + 15) >> 4;
+  int* gpage = reinterpret_cast<int*>(sh.cand);     // the candidate list is free until the selection
+  const int32_t* bt = bv.block_table + (int64_t)b * bv.max_pages_per_seq;
+  for (int i = tid; i < kTkBins; i += kThreads) sh.hist[i] = 0;
+  for (int i = tid; i < ngroups; i += kThreads) gpage[i] = bt[(base + 16 * i) / P];   // < visible <= pages * P
+
+  // q as four 16-head A operands and the head gates in accumulator order
+  // (lane (c, g) holds rows 4g + i of each 16-head tile)
+  const uint8_t* qr = p.q8 + (int64_t)t * (kIdxHeads * kIdxDim);
+  i32x8 qa[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) qa[m] = *reinterpret_cast<const i32x8*>(qr + (16 * m + c) * kIdxDim + 32 * g);
+  float wv[16];
+  const float* wrow = p.w + (int64_t)t * kIdxHeads;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const f32x4 w4 = *reinterpret_cast<const f32x4*>(wrow + 16 * m + 4 * g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[4 * m + i] = w4[i];
+  }
+  const int n_init = min(p.num_init, vis);
+  const int local0 = max(vis - p.num_local, n_init);  // forced: [0, n_init) and [local0, vis)
+  __syncthreads();                                    // page list and cleared histogram
+
+  const int64_t scale_off = (int64_t)P * kIdxDim;
+  const int nb = (ngroups + 3) >> 2;                  // batches of four groups
+  // Batch j: the key operands of its four groups (groups past the chunk
+  // re-read its last group) and, for lane (c, g), the scale and page
+  // validity of key c of group g, the key this lane scores.
+  auto load = [&](int j, i32x8 (&kb)[4], float& sgl, int& okl) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int gi = min(4 * j + u, ngroups - 1);
+      const int pid = __builtin_amdgcn_readfirstlane(gpage[gi]);
+      const bool okp = pid >= 0 && pid < bv.num_pages;
+      const uint8_t* pg = p.cache + (int64_t)(okp ? pid : 0) * p.page_bytes;
+      const int slot = (base + 16 * gi) % P + c;     // < P: base and P are multiples of 16
+      kb[u] = *reinterpret_cast<const i32x8*>(pg + (int64_t)slot * kIdxDim + 32 * g);
+    }
+    const int gl = min(4 * j + g, ngroups - 1);
+    const int pl = gpage[gl];
+    okl = pl >= 0 && pl < bv.num_pages;
+    const uint8_t* pg = p.cache + (int64_t)(okl ? pl : 0) * p.page_bytes;
+    sgl = *reinterpret_cast<const float*>(pg + scale_off + 4 * ((base + 16 * gl) % P + c));
+  };
+  // Ring of kFuAhead + 1 slots: batch j0 + r * waves sits in slot r. The
+  // slots rotate by name (the inner loop is unrolled), never by register
+  // copies: a copy of a register that a load in flight writes would wait for
+  // that load. Every prefetch is issued, past the end as a re-read of the
+  // last batch: after a conditional load the compiler can no longer count the
+  // loads in flight and waits for all of them. Either way the prefetch would
+  // stop overlapping the contraction.
+  i32x8 kb[kFuAhead + 1][4];
+  float sg[kFuAhead + 1];
+  int ok[kFuAhead + 1];
+#pragma unroll
+  for (int d = 0; d < kFuAhead; ++d) load(min(wave + d * kWaves, nb - 1), kb[d], sg[d], ok[d]);
+  auto score = [&](int j, const i32x8 (&kbj)[4], float sgj, int okj) {
+    float part[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      part[u] = 0.f;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const f32x4 acc = mfma_fp8_16x16x128(qa[m], kbj[u], zero);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part[u] = fmaf(wv[4 * m + i], relu_bits(acc[i]), part[u]);
+      }
+    }
+    // lane (c, g): key c of group g of the batch
+    const float v = sum_scatter_over_groups(part[0], part[1], part[2], part[3]);
+    const int pos = 16 * (4 * j + g) + c;              // chunk position
+    if (pos < n) {
+      const int s = base + pos;
+      float val = okj ? v * sgj : -INFINITY;
+      if (s < n_init || s >= local0) val = INFINITY;
+      const uint32_t key = ordered_key(val);
+      sh.keys[kslot(pos)] = key;
+      atomicAdd(&sh.hist[key >> 20], 1u);
+    }
+  };
+  // The slots of an outer step past the last batch compute on re-read data
+  // and store nothing (their positions are past the chunk); skipping them
+  // would make the waits above conservative again.
+  for (int j0 = wave; j0 < nb; j0 += (kFuAhead + 1) * kWaves) {
+#pragma unroll
+    for (int r = 0; r <= kFuAhead; ++r) {
+      const int j = j0 + r * kWaves;
+      const int jl = j + kFuAhead * kWaves;           // into the slot batch j - waves left
+      constexpr int kSlots = kFuAhead + 1;
+      const int sl = (r + kFuAhead) % kSlots;
+      load(min(jl, nb - 1), kb[sl], sg[sl], ok[sl]);
+      score(j, kb[r], sg[r], ok[r]);
+    }
+  }
+  __syncthreads();
+}
+
+template <int kMode, int kThreads>
+__global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
   constexpr bool kKeys = kMode == kMerge;             // the source holds keys, not logits
-  __shared__ TopkShared sh;
+  constexpr int kWaves = TopkShared<kThreads>::kWaves;
+  constexpr int kCache = TopkShared<kThreads>::kCache;
+  constexpr int kCand = TopkShared<kThreads>::kCand;
+  __shared__ TopkShared<kThreads> sh;
   const BatchView& bv = p.batch;
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
@@ -165,12 +308,12 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
   const int n_row = visible_keys(bv.seq_lens_k[b], q_len, j, cap);
   const int k = p.k;
   int32_t* out = p.topk_idx + (int64_t)t * k;
-  const int64_t cand0 = ((int64_t)t * p.chunks + (kMode == kChunk ? blockIdx.y : 0)) * k;
+  const int64_t cand0 = ((int64_t)t * p.chunks + ((kMode == kChunk || kMode == kFused) ? blockIdx.y : 0)) * k;
 
   // this selection: elements [0, n) of `src`
   int n = n_row;
   int base = 0;                                       // chunk: position of element 0
-  const void* src = p.logits + (int64_t)t * p.stride;
+  const void* src = p.logits ? p.logits + (int64_t)t * p.stride : nullptr;   // fused: no logits
   if (kMode == kChunk) {
     if (n_row <= k) return;                           // short rows are the merge's
     base = (int)blockIdx.y * p.chunk;
@@ -178,8 +321,21 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
     n = min(p.chunk, n_row - base);
     src = p.logits + (int64_t)t * p.stride + base;
     if (n <= k) {                                     // the whole chunk is a candidate
-      for (int i = tid; i < n; i += kTkThreads) {
+      for (int i = tid; i < n; i += kThreads) {
         p.cand_key[cand0 + i] = src_key<false>(src, i);
+        p.cand_pos[cand0 + i] = base + i;
+      }
+      return;
+    }
+  } else if (kMode == kFused) {
+    if (n_row <= k) return;                           // short rows are the merge's
+    base = (int)blockIdx.y * p.chunk;
+    if (base >= n_row) return;
+    n = min(p.chunk, n_row - base);
+    fused_scores<kThreads>(p, sh, t, b, base, n, n_row);
+    if (n <= k) {                                     // the whole chunk is a candidate
+      for (int i = tid; i < n; i += kThreads) {
+        p.cand_key[cand0 + i] = sh.keys[kslot(i)];
         p.cand_pos[cand0 + i] = base + i;
       }
       return;
@@ -191,48 +347,49 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
     }
     src = p.cand_key + cand0;
   }
-  if (n <= k) {  // short row (or as many candidates as winners): every element, in order, then -1
-    for (int i = tid; i < k; i += kTkThreads)
+  if (kMode != kFused && n <= k) {  // short row (or as many candidates as winners): every element, in order, then -1
+    for (int i = tid; i < k; i += kThreads)
       out[i] = i < n ? (kMode == kMerge && n_row > k ? p.cand_pos[cand0 + i] : i) : -1;
     return;
   }
 
-  const bool cached = n <= kTkCache;
-  for (int i = tid; i < kTkBins; i += kTkThreads) sh.hist[i] = 0;
-  __syncthreads();
-
-  // ---- level 0 (bits 31..20) while reading the row once ----
-  const bool vec = ((reinterpret_cast<uintptr_t>(src) & 15u) == 0);
-  const int n4 = vec ? n / 4 : 0;
-  for (int i0 = 0; i0 < n4; i0 += kTkThreads * kTkLoadUnroll) {
-    i32x4 v[kTkLoadUnroll];
+  const bool cached = kMode == kFused || n <= kCache;
+  // ---- level 0 (bits 31..20) while reading the row once (fused: done with the scores) ----
+  if (kMode != kFused) {
+    for (int i = tid; i < kTkBins; i += kThreads) sh.hist[i] = 0;
+    __syncthreads();
+    const bool vec = ((reinterpret_cast<uintptr_t>(src) & 15u) == 0);
+    const int n4 = vec ? n / 4 : 0;
+    for (int i0 = 0; i0 < n4; i0 += kThreads * kTkLoadUnroll) {
+      i32x4 v[kTkLoadUnroll];
 #pragma unroll
-    for (int u = 0; u < kTkLoadUnroll; ++u) {
-      int i4 = i0 + u * kTkThreads + tid;
-      i4 = i4 < n4 ? i4 : n4 - 1;               // clamped: always in bounds
-      v[u] = static_cast<const i32x4*>(src)[i4];
-    }
+      for (int u = 0; u < kTkLoadUnroll; ++u) {
+        int i4 = i0 + u * kThreads + tid;
+        i4 = i4 < n4 ? i4 : n4 - 1;               // clamped: always in bounds
+        v[u] = static_cast<const i32x4*>(src)[i4];
+      }
 #pragma unroll
-    for (int u = 0; u < kTkLoadUnroll; ++u) {
-      const int i4 = i0 + u * kTkThreads + tid;
-      if (i4 < n4) {
-        uint32_t kk[4];
+      for (int u = 0; u < kTkLoadUnroll; ++u) {
+        const int i4 = i0 + u * kThreads + tid;
+        if (i4 < n4) {
+          uint32_t kk[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kk[e] = kKeys ? (uint32_t)v[u][e] : ordered_key(__int_as_float(v[u][e]));
-          atomicAdd(&sh.hist[kk[e] >> 20], 1u);
+          for (int e = 0; e < 4; ++e) {
+            kk[e] = kKeys ? (uint32_t)v[u][e] : ordered_key(__int_as_float(v[u][e]));
+            atomicAdd(&sh.hist[kk[e] >> 20], 1u);
+          }
+          if (cached)
+            *reinterpret_cast<i32x4*>(sh.keys + kslot(4 * i4)) = i32x4{(int)kk[0], (int)kk[1], (int)kk[2], (int)kk[3]};
         }
-        if (cached)
-          *reinterpret_cast<i32x4*>(sh.keys + kslot(4 * i4)) = i32x4{(int)kk[0], (int)kk[1], (int)kk[2], (int)kk[3]};
       }
     }
+    for (int i = 4 * n4 + tid; i < n; i += kThreads) {
+      const uint32_t kk = src_key<kKeys>(src, i);
+      if (cached) sh.keys[kslot(i)] = kk;
+      atomicAdd(&sh.hist[kk >> 20], 1u);
+    }
+    __syncthreads();
   }
-  for (int i = 4 * n4 + tid; i < n; i += kTkThreads) {
-    const uint32_t kk = src_key<kKeys>(src, i);
-    if (cached) sh.keys[kslot(i)] = kk;
-    atomicAdd(&sh.hist[kk >> 20], 1u);
-  }
-  __syncthreads();
   uint32_t need = (uint32_t)k;
   uint32_t bin, above;
   select_bin(sh, kTkBins, need, 0, &bin, &above);
@@ -241,9 +398,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
 
   // ---- level 1 (bits 19..8) among keys whose top 12 bits equal the prefix;
   //      those keys are also collected (unordered) for the last level ----
-  const bool keep = sh.hist[prefix] <= (uint32_t)kTkCand;   // read before the histogram is cleared
+  const bool keep = sh.hist[prefix] <= (uint32_t)kCand;   // read before the histogram is cleared
   __syncthreads();
-  for (int i = tid; i < kTkBins; i += kTkThreads) sh.hist[i] = 0;
+  for (int i = tid; i < kTkBins; i += kThreads) sh.hist[i] = 0;
   if (tid == 0) sh.n_cand = 0;
   __syncthreads();
   // Each wave appends its matches to its own 252 slots of the list (ballot and
@@ -265,8 +422,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
     // so the rounds of the whole pass number the most matches of one lane.
     uint32_t mm = 0;
 #pragma unroll
-    for (int j = 0; j < kTkCache / (kTkPer * kTkThreads); ++j) {
-      const int i = kTkPer * tid + kTkPer * kTkThreads * j;
+    for (int j = 0; j < kCache / (kTkPer * kThreads); ++j) {
+      const int i = kTkPer * tid + kTkPer * kThreads * j;
       if (i < n) {
         uint32_t u[kTkPer];
         load8<kKeys>(src, sh, true, n, i, u);
@@ -280,12 +437,12 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
       if (m) {
         const int b = __builtin_ctz(mm);
         mm &= mm - 1u;
-        x = sh.keys[kslot(kTkPer * tid + kTkPer * kTkThreads * (b / kTkPer) + b % kTkPer)];
+        x = sh.keys[kslot(kTkPer * tid + kTkPer * kThreads * (b / kTkPer) + b % kTkPer)];
       }
       take_match(m, x);
     }
   }
-  for (int i = kTkPer * tid; !cached && i < n; i += kTkPer * kTkThreads) {
+  for (int i = kTkPer * tid; !cached && i < n; i += kTkPer * kThreads) {
     uint32_t u[kTkPer];
     load8<kKeys>(src, sh, cached, n, i, u);
     // matches are rare: each round handles one match per lane, so a wave issues
@@ -313,11 +470,11 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
   need -= above;
 
   // ---- level 2 (bits 7..0) among keys whose top 24 bits equal the prefix ----
-  for (int i = tid; i < 256; i += kTkThreads) sh.hist[i] = 0;
+  for (int i = tid; i < 256; i += kThreads) sh.hist[i] = 0;
   __syncthreads();
   bool kept = keep;
 #pragma unroll
-  for (int w = 0; w < kTkWaves; ++w) kept = kept && sh.wave_cand[w] <= (uint32_t)kTkCandPerWave;
+  for (int w = 0; w < kWaves; ++w) kept = kept && sh.wave_cand[w] <= (uint32_t)kTkCandPerWave;
   if (kept) {
     const uint32_t nc = sh.wave_cand[wave];            // wave w scans wave w's slots
     for (uint32_t i = lane_id(); i < nc; i += kWave) {
@@ -325,7 +482,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
       if ((u >> 8) == prefix) atomicAdd(&sh.hist[u & 0xffu], 1u);
     }
   } else {
-    for (int i = kTkPer * tid; i < n; i += kTkPer * kTkThreads) {
+    for (int i = kTkPer * tid; i < n; i += kTkPer * kThreads) {
       uint32_t u[kTkPer];
       load8<kKeys>(src, sh, cached, n, i, u);
 #pragma unroll
@@ -343,7 +500,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
   // p) + min(#keys == thr before p, need). Thread tid owns a run of
   // consecutive positions, handled 32 at a time as bit masks: count its winners,
   // one block-wide scan, then place them in order.
-  const int run_len = cached ? kTkRun : ((n + kTkThreads - 1) / kTkThreads + 31) & ~31;
+  const int run_len = cached ? kTkRun : ((n + kThreads - 1) / kThreads + 31) & ~31;
   const int run0 = run_len * tid;
   // masks of the keys > thr and == thr among positions [p0, p0 + 32)
   auto masks32 = [&](int p0, uint32_t* gtm, uint32_t* eqm) {
@@ -423,11 +580,11 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkParams p) {
   // histogram area, free since the last bin selection; they leave in
   // consecutive, coalesced stores instead of each thread's scattered ones.
   __syncthreads();
-  for (int i = tid; i < k; i += kTkThreads) {
+  for (int i = tid; i < k; i += kThreads) {
     const int e = (int)sh.hist[i];
     if (kMode == kWholeRow) {
       out[i] = e;
-    } else if (kMode == kChunk) {
+    } else if (kMode == kChunk || kMode == kFused) {
       p.cand_key[cand0 + i] = cached ? sh.keys[kslot(e)] : src_key<false>(src, e);
       p.cand_pos[cand0 + i] = base + e;
     } else {
@@ -466,13 +623,48 @@ size_t topk_workspace_bytes(int num_rows, int max_len, int k) {
 hipError_t launch_topk(const TopkParams& p, hipStream_t s) {
   if (p.batch.num_rows == 0) return hipSuccess;
   if (p.chunk == 0) {
-    hipLaunchKernelGGL(topk_kernel<kWholeRow>, dim3(p.batch.num_rows), dim3(kTkThreads), 0, s, p);
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(topk_kernel<kWholeRow, kTkThreads>), dim3(p.batch.num_rows), dim3(kTkThreads),
+                       0, s, p);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(topk_kernel<kChunk>, dim3(p.batch.num_rows, p.chunks), dim3(kTkThreads), 0, s, p);
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(topk_kernel<kChunk, kTkThreads>), dim3(p.batch.num_rows, p.chunks),
+                     dim3(kTkThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_kernel<kMerge>, dim3(p.batch.num_rows), dim3(kTkThreads), 0, s, p);
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(topk_kernel<kMerge, kTkThreads>), dim3(p.batch.num_rows), dim3(kTkThreads),
+                     0, s, p);
+  return hipGetLastError();
+}
+
+int indexer_topk_chunk(int num_rows, int max_len, int k) {
+  // Chunks fill the fused work-group's key cache (8192 keys). With k at most a
+  // quarter of that, chunks of 4096 when 8192 would leave fewer than two
+  // work-groups per CU: phase one then spreads over more CUs, for twice the
+  // candidates per chunk's keys, as long as a row's candidates still fit the
+  // merge's LDS key cache. A chunk is never shorter than k, so every chunk but
+  // a row's last gives exactly k candidates.
+  const int64_t wgs = (int64_t)num_rows * ((max_len + kFuCache - 1) / kFuCache);
+  const int64_t cands_half = (int64_t)((max_len + kFuCache / 2 - 1) / (kFuCache / 2)) * k;
+  if (4 * k <= kFuCache && wgs < 512 && cands_half <= kTkCache) return kFuCache / 2;
+  return kFuCache;
+}
+
+size_t indexer_topk_workspace_bytes(int num_rows, int max_len, int k) {
+  const int chunk = indexer_topk_chunk(num_rows, max_len, k);
+  const int chunks = (max_len + chunk - 1) / chunk;
+  return (size_t)num_rows * chunks * k * (sizeof(uint32_t) + sizeof(int32_t));
+}
+
+hipError_t launch_indexer_topk(const TopkParams& p, hipStream_t s) {
+  if (p.batch.num_rows == 0) return hipSuccess;
+  if (p.chunks > 0) {
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(topk_kernel<kFused, kFuThreads>), dim3(p.batch.num_rows, p.chunks),
+                       dim3(kFuThreads), 0, s, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(topk_kernel<kMerge, kTkThreads>), dim3(p.batch.num_rows), dim3(kTkThreads),
+                     0, s, p);
   return hipGetLastError();
 }
 

@@ -292,3 +292,53 @@ def test_noalloc_reports_the_plain_calls_status(L):
     assert L.sparse_mla_decode(*args, V(0x1000), 1 << 20, None) == dsa.DSA_ERR_UNSUPPORTED
     bad = args[:5] + (0,) + args[6:]                      # k = 0
     assert L.sparse_mla_decode_noalloc(*bad, None) == dsa.DSA_ERR_INVALID_ARGUMENT
+
+
+def _fused(L, batch, H=64, D=128, k=2048, n_init=0, n_local=0, ws=0x600, wsb=1 << 30, q=0x100, w=0x200,
+           cache=0x300, idx=0x400):
+    V = ctypes.c_void_p
+    return L.dsa_indexer_topk(ctypes.byref(batch), V(q) if q else None, V(w) if w else None,
+                              V(cache) if cache else None, H, D, n_init, n_local, k, V(idx) if idx else None,
+                              V(ws) if ws else None, wsb, None)
+
+
+def test_fused_indexer_topk_validation(L):
+    b = _batch()
+    assert _fused(L, b, H=32) == dsa.DSA_ERR_UNSUPPORTED
+    assert _fused(L, b, D=64) == dsa.DSA_ERR_UNSUPPORTED
+    for k in (0, -3, 4097):
+        assert _fused(L, b, k=k) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert _fused(L, b, n_init=-1) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert _fused(L, b, n_local=-1) == dsa.DSA_ERR_INVALID_ARGUMENT
+    for which in ("q", "w", "cache", "idx"):
+        assert _fused(L, b, **{which: 0}) == dsa.DSA_ERR_INVALID_ARGUMENT, which
+    for which in ("q", "w", "cache"):
+        assert _fused(L, b, **{which: 0x108}) == dsa.DSA_ERR_INVALID_ARGUMENT, which
+    assert _fused(L, _batch(page_size=24)) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert _fused(L, _batch(max_seq_len_k=(1 << 24) + 1)) == dsa.DSA_ERR_UNSUPPORTED
+    assert _fused(L, b, H=16) == dsa.DSA_ERR_UNSUPPORTED
+    assert "64 fp8 heads" in _last(L)
+    # an empty batch needs nothing and launches nothing
+    empty = _batch(num_seqs=0, num_rows=0, block_table=None, seq_lens_k=None)
+    assert _fused(L, empty, ws=0, wsb=0, q=0, w=0, cache=0, idx=0) == dsa.DSA_OK
+
+
+def _last(L):
+    return L.dsa_last_error().decode()
+
+
+def test_fused_indexer_topk_workspace(L):
+    # 64 rows of up to 32,564 keys: 8,192-key chunks would give 256 work-groups
+    # (fewer than two per CU), so chunks of 4,096: 8 per row, k pairs of 8 bytes each
+    b = _batch(num_seqs=64, num_rows=64, max_pages_per_seq=509, max_seq_len_k=32564)
+    need = L.dsa_workspace_bytes(dsa.DSA_OP_INDEXER_TOPK, ctypes.byref(b), 2048, 0, 0, 0)
+    assert need == 64 * 8 * 2048 * 8
+    assert _fused(L, b, wsb=need - 1) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
+    assert _fused(L, b, ws=0, wsb=need) == dsa.DSA_ERR_INVALID_ARGUMENT
+    # 4,096 prefill rows of up to 20,480 keys: chunks of 8,192 (3 per row)
+    pre = _batch(num_seqs=1, num_rows=4096, max_pages_per_seq=320, max_seq_len_k=20480, max_seq_len_q=4096,
+                 cu_seqlens_q=0x7000)
+    assert L.dsa_workspace_bytes(dsa.DSA_OP_INDEXER_TOPK, ctypes.byref(pre), 2048, 0, 0, 0) == 4096 * 3 * 2048 * 8
+    # k above a quarter of 8,192 keeps the 8,192-key chunks
+    assert L.dsa_workspace_bytes(dsa.DSA_OP_INDEXER_TOPK, ctypes.byref(b), 4096, 0, 0, 0) == 64 * 4 * 4096 * 8
+    assert L.dsa_workspace_bytes(dsa.DSA_OP_INDEXER_TOPK, ctypes.byref(b), 0, 0, 0, 0) == ctypes.c_size_t(-1).value
