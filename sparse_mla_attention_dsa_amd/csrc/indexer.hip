@@ -135,7 +135,9 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_fp8_kernel(IndexerPara
 // a CU issues first (which run ahead) take more of them and the CU's waves
 // finish together. A wave issues the loads of its next chunk before the MFMAs
 // of the current one, and each key group meets the q of every row of its
-// unit; q and the head weights are reloaded when the unit changes.
+// unit; q and the head weights are reloaded when the unit changes. After the
+// MFMAs of a chunk the four groups' head sums are reduce-scattered over the
+// lane groups, so each row gets one 64-lane store per chunk.
 constexpr int kStreamMaxUnits = 1024;
 constexpr int kStreamBatch = 4;                                  // groups per chunk
 constexpr int kStreamMaxQLen = 4;                                // rows per request, multi-row units
@@ -253,8 +255,9 @@ __global__ __launch_bounds__((stream_waves<kR, kAhead>() * kWave)) void indexer_
     if (lane == 0) v = atomicAdd(&next_chunk, 1);
     return __builtin_amdgcn_readfirstlane(v);
   };
-  // key operands (lane (c, g): key 16u + c of the chunk, bytes [32g, 32g + 32)) and scales
-  auto load_batch = [&](const Batch& x, i32x8 (&kb)[kStreamBatch], float (&sg)[kStreamBatch]) {
+  // key operands (lane (c, g): key 16u + c of the chunk, bytes [32g, 32g + 32))
+  // and, for lane (c, g), the scale of key 16g + c, the key this lane writes
+  auto load_batch = [&](const Batch& x, i32x8 (&kb)[kStreamBatch], float& sgl) {
     const bool okp = x.page >= 0 && x.page < bv.num_pages;
     const uint8_t* pg = cache + (int64_t)(okp ? x.page : 0) * p.page_bytes;
 #pragma unroll
@@ -262,8 +265,9 @@ __global__ __launch_bounds__((stream_waves<kR, kAhead>() * kWave)) void indexer_
       const int uu = u < x.cnt ? u : 0;                          // past the chunk: re-read group 0
       const int slot = (16 * (x.gi + uu)) % P + c;
       kb[u] = *reinterpret_cast<const i32x8*>(pg + (int64_t)slot * kIdxDim + 32 * g);
-      sg[u] = *reinterpret_cast<const float*>(pg + scale_off + 4 * slot);
     }
+    const int gl = g < x.cnt ? g : 0;
+    sgl = *reinterpret_cast<const float*>(pg + scale_off + 4 * ((16 * (x.gi + gl)) % P + c));
   };
 
   // q of the unit's rows as 16-head A operands (lane (c, g): head 16m + c,
@@ -316,63 +320,72 @@ __global__ __launch_bounds__((stream_waves<kR, kAhead>() * kWave)) void indexer_
     if (tid == 0) next_chunk = 0;
     __syncthreads();
 
-    // ---- the waves take chunks until the round is done: a wave holds the
-    // chunk it computes and the kAhead after it (their loads in flight during
-    // the MFMAs), and takes the next one during the MFMAs ----
-    i32x8 kb[kAhead + 1][kStreamBatch];
-    float sg[kAhead + 1][kStreamBatch];
-    Batch bq[kAhead + 1] = {};
-    int jq[kAhead + 1];
-#pragma unroll
-    for (int d = 0; d <= kAhead; ++d) {
-      jq[d] = (d == 0 || jq[d - 1] < n) ? take() : n;
-      if (jq[d] < n) {
-        bq[d] = record(jq[d]);
-        load_batch(bq[d], kb[d], sg[d]);
-      }
-    }
-    while (jq[0] < n) {
-      int jt = n;                                                // read after the MFMAs
-      if (lane == 0 && jq[kAhead] < n) jt = atomicAdd(&next_chunk, 1);
-      const Batch cur = bq[0];
-      if (cur.t != q_unit) load_unit(cur);
-      // ---- logits of the chunk, for every row of its unit ----
-      const bool okp = cur.page >= 0 && cur.page < bv.num_pages;
+    // ---- the waves take chunks until the round is done. Two chunk slots,
+    // A and B, alternate by name: while the MFMAs of one slot's chunk run,
+    // the other slot's loads are in flight, and the index of the chunk after
+    // that is taken. Every slot load is issued (once the round is out of
+    // chunks, as a re-read of the chunk just computed), and no register of a
+    // load in flight is copied: either would make the compiler wait for every
+    // load in flight before the MFMAs. ----
+    static_assert(kAhead == 1, "the stream loop holds two chunk slots");
+    // logits of chunk x for every row of its unit: the four groups' head sums
+    // are reduce-scattered so that lane (c, g) writes key 16g + c of the chunk
+    auto compute = [&](const Batch& x, const i32x8 (&kb)[kStreamBatch], float sgl) {
+      const bool okp = x.page >= 0 && x.page < bv.num_pages;
 #pragma unroll
       for (int r = 0; r < kR; ++r) {
-        if (r >= cur.nr) break;
+        if (r >= x.nr) break;
         // rows of a unit see one key more each; the last one sees vl
-        const int vis = (r == cur.nr - 1) ? cur.vl : cur.vf;
-        float* out = p.logits + (int64_t)(cur.r0 + r) * p.stride;
+        const int vis = (r == x.nr - 1) ? x.vl : x.vf;
+        float part[kStreamBatch];
 #pragma unroll
         for (int u = 0; u < kStreamBatch; ++u) {
-          if (u >= cur.cnt) break;
           const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-          float part = 0.f;
+          part[u] = 0.f;
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
-            const f32x4 acc = mfma_fp8_16x16x128(qa[r][m], kb[0][u], zero);
+            const f32x4 acc = mfma_fp8_16x16x128(qa[r][m], kb[u], zero);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) part = fmaf(wv[r][4 * m + i], relu_bits(acc[i]), part);
+            for (int i = 0; i < 4; ++i) part[u] = fmaf(wv[r][4 * m + i], relu_bits(acc[i]), part[u]);
           }
-          part = sum_over_groups(part);
-          const int s = 16 * (cur.gi + u) + c;
-          if (g == 0 && s < vis) out[s] = okp ? part * sg[0][u] : -INFINITY;
         }
+        const float tot = sum_scatter_over_groups(part[0], part[1], part[2], part[3]);
+        // one store per row for the whole wave, through a buffer resource over
+        // the row: lanes past the chunk or the row get an offset out of range,
+        // which drops their store (a branch around the store would make the
+        // number of stores in flight unknown to the compiler's waits)
+        const int s = 16 * (x.gi + g) + c;
+        const __amdgpu_buffer_rsrc_t row = __builtin_amdgcn_make_buffer_rsrc(
+            p.logits + (int64_t)(x.r0 + r) * p.stride, (short)0, (int)(p.stride * 4), 0x00020000);
+        const uint32_t off = (g < x.cnt && s < vis) ? 4u * (uint32_t)s : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(okp ? tot * sgl : -INFINITY), row, (int)off, 0, 0);
       }
-      const int tail = jq[kAhead];
-#pragma unroll
-      for (int d = 0; d < kAhead; ++d) {
-        bq[d] = bq[d + 1];
-        jq[d] = jq[d + 1];
-#pragma unroll
-        for (int u = 0; u < kStreamBatch; ++u) { kb[d][u] = kb[d + 1][u]; sg[d][u] = sg[d + 1][u]; }
-      }
-      jq[kAhead] = tail < n ? __builtin_amdgcn_readfirstlane(jt) : n;
-      if (jq[kAhead] < n) {
-        bq[kAhead] = record(jq[kAhead]);
-        load_batch(bq[kAhead], kb[kAhead], sg[kAhead]);
-      }
+    };
+    static_assert(kStreamBatch == 4, "one group per lane group");
+    i32x8 kbA[kStreamBatch], kbB[kStreamBatch];
+    float sgA, sgB;
+    int ja = take();
+    Batch ba = record(ja < n ? ja : 0), bb = ba;
+    load_batch(ba, kbA, sgA);
+    int jb = ja < n ? take() : n;
+    while (ja < n) {
+      // slot A computes chunk ja while slot B loads chunk jb
+      int jt = n;                                                // read after the MFMAs
+      if (lane == 0 && jb < n) jt = atomicAdd(&next_chunk, 1);
+      if (ba.t != q_unit) load_unit(ba);
+      bb = record(jb < n ? jb : ja);
+      load_batch(bb, kbB, sgB);
+      compute(ba, kbA, sgA);
+      ja = jb < n ? __builtin_amdgcn_readfirstlane(jt) : n;
+      if (jb >= n) break;
+      // slot B computes chunk jb while slot A loads chunk ja
+      jt = n;
+      if (lane == 0 && ja < n) jt = atomicAdd(&next_chunk, 1);
+      if (bb.t != q_unit) load_unit(bb);
+      ba = record(ja < n ? ja : jb);
+      load_batch(ba, kbA, sgA);
+      compute(bb, kbB, sgB);
+      jb = ja < n ? __builtin_amdgcn_readfirstlane(jt) : n;
     }
     __syncthreads();                                             // records free for the next round
   }
