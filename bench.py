@@ -13,7 +13,8 @@ resident. Prints one JSON line:
   per byte is above the MFMA ridge) per launch over its average launch time,
   against the MI355X peak;
 * extra: the same step on further workloads (by default the batch-64 decode
-  with every context at 32,768 keys, the literal "ctx 32k" of the metric);
+  with every context at 32,768 keys, the literal "ctx 32k" of the metric, and
+  the ragged batch with the fused indexer + top-k call);
 * cpu_baseline: the float64 oracle timed on a bounded sample of the same
   workload on this host's cores.
 """
@@ -367,8 +368,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_b64_ragged")
-    ap.add_argument("--extra-workloads", default="decode_b64_32k",
-                    help="comma-separated workloads also timed and reported under `extra` ('' for none)")
+    ap.add_argument("--extra-workloads", default="decode_b64_32k,decode_b64_ragged:fused",
+                    help="comma-separated workloads also timed and reported under `extra` ('' for none); "
+                         "NAME:fused or NAME:two-call picks the selection path")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch the timed steps eagerly")
     ap.add_argument("--fused", action="store_true",
@@ -423,12 +425,18 @@ def main():
         "roofline": m["roofline"],
     }
     extra = {}
-    for name in [x for x in args.extra_workloads.split(",") if x and x != cfg.name]:
+    for spec in [x for x in args.extra_workloads.split(",") if x]:
+        # NAME, or NAME:fused / NAME:two-call to choose the selection path
+        name, _, path = spec.partition(":")
+        fused_x = args.fused if not path else path == "fused"
+        if name == cfg.name and fused_x == args.fused:
+            continue
         del wl
         torch.cuda.empty_cache()
         wl_x, mx = measure(CONFIGS[name], args.steps, args.warmup, graph=not args.no_graph,
-                           with_input_side=False, fused=args.fused)
-        extra[name] = {"tokens_per_s": mx["tokens_per_s"], "ms_per_step": mx["ms_per_step"],
+                           with_input_side=False, fused=fused_x)
+        extra[spec] = {"tokens_per_s": mx["tokens_per_s"], "ms_per_step": mx["ms_per_step"],
+                       "selection": "dsa_indexer_topk" if fused_x else "dsa_indexer_logits + dsa_topk",
                        "description": CONFIGS[name].note, "ctx_total": int(wl_x.seq_lens_k.sum()),
                        "sparse_attn_hbm_gbps": mx["stages"]["sparse_mla"]["hbm_gbps"],
                        "stages": {k: {kk: v[kk] for kk in ("us", "bound", "hbm_frac", "mfma_frac") if kk in v}
