@@ -27,7 +27,11 @@
 // the k-th largest are appended (wave-aggregated) to a candidate list for the
 // last digit. The ordered output gives each thread one contiguous run of
 // positions: count winners in the run, one block-wide scan, place the run's
-// winners in order in LDS, then write the row out with coalesced stores.
+// winners in order in LDS, then write the row out with coalesced stores. For
+// selections held in LDS the middle pass reads each thread's output run and
+// keeps two masks of it (first digit above the prefix, equal to it), so the
+// output pass compares only the run's positions in the prefix bin with the
+// exact k-th key.
 //
 // Fused with the scores (dsa_indexer_topk): phase one runs in work-groups of
 // 256 threads, one per (row, chunk of up to 8192 keys), three per CU. Each
@@ -416,28 +420,36 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
     if (keep && m && slot < (uint32_t)kTkCandPerWave) sh.cand[wave * kTkCandPerWave + slot] = x;
     wcnt += (uint32_t)__builtin_popcountll(mask);
   };
+  // cached selections: masks of the thread's output run [32 tid, 32 tid + 32)
+  // with a first digit above the prefix and equal to it, kept for the output
+  uint32_t above_run = 0, inbin_run = 0;
   if (cached) {
-    // The thread's (at most 32) positions i = 8 tid + 8192 j + e first give
-    // one match mask; the matches are then handled in rounds of one per lane,
-    // so the rounds of the whole pass number the most matches of one lane.
+    // The run's positions first give the two masks; the matches are then
+    // handled in rounds of one per lane, so the rounds of the whole pass
+    // number the most matches of one lane.
+    const int r0 = kTkRun * tid;
     uint32_t mm = 0;
+    if (r0 < n) {
 #pragma unroll
-    for (int j = 0; j < kCache / (kTkPer * kThreads); ++j) {
-      const int i = kTkPer * tid + kTkPer * kThreads * j;
-      if (i < n) {
-        uint32_t u[kTkPer];
-        load8<kKeys>(src, sh, true, n, i, u);
+      for (int q = 0; q < kTkRun / 4; ++q) {
+        const i32x4 a = *reinterpret_cast<const i32x4*>(sh.keys + kslot(r0 + 4 * q));
 #pragma unroll
-        for (int e = 0; e < kTkPer; ++e) mm |= ((i + e < n && (u[e] >> 20) == prefix) ? 1u : 0u) << (kTkPer * j + e);
+        for (int e = 0; e < 4; ++e) {
+          const bool valid = r0 + 4 * q + e < n;
+          const uint32_t d = (uint32_t)a[e] >> 20;
+          mm |= (valid && d == prefix ? 1u : 0u) << (4 * q + e);
+          above_run |= (valid && d > prefix ? 1u : 0u) << (4 * q + e);
+        }
       }
     }
+    inbin_run = mm;
     while (__ballot(mm != 0u)) {
       const bool m = mm != 0u;
       uint32_t x = 0;
       if (m) {
-        const int b = __builtin_ctz(mm);
+        const int e = __builtin_ctz(mm);
         mm &= mm - 1u;
-        x = sh.keys[kslot(kTkPer * tid + kTkPer * kThreads * (b / kTkPer) + b % kTkPer)];
+        x = sh.keys[kslot(r0 + e)];
       }
       take_match(m, x);
     }
@@ -503,23 +515,14 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
   const int run_len = cached ? kTkRun : ((n + kThreads - 1) / kThreads + 31) & ~31;
   const int run0 = run_len * tid;
   // masks of the keys > thr and == thr among positions [p0, p0 + 32)
-  auto masks32 = [&](int p0, uint32_t* gtm, uint32_t* eqm) {
+  auto masks32 = [&](int p0, uint32_t* gtm, uint32_t* eqm) {   // selections read from memory
     uint32_t key[32];
-    if (cached) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const i32x4 a = *reinterpret_cast<const i32x4*>(sh.keys + kslot(p0 + 4 * j));
+    for (int j = 0; j < 4; ++j) {
+      uint32_t u[kTkPer];
+      load8<kKeys>(src, sh, false, n, p0 + 8 * j, u);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) key[4 * j + e] = (uint32_t)a[e];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint32_t u[kTkPer];
-        load8<kKeys>(src, sh, false, n, p0 + 8 * j, u);
-#pragma unroll
-        for (int e = 0; e < kTkPer; ++e) key[8 * j + e] = u[e];
-      }
+      for (int e = 0; e < kTkPer; ++e) key[8 * j + e] = u[e];
     }
     uint32_t g = 0, q = 0;
 #pragma unroll
@@ -534,13 +537,27 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
   };
   uint32_t cgt = 0, ceq = 0;
   uint32_t gtm0 = 0, eqm0 = 0;                          // cached rows: the run's only block, kept for the write
-  for (int p0 = run0; p0 < run0 + run_len && p0 < n; p0 += 32) {
-    uint32_t gtm, eqm;
-    masks32(p0, &gtm, &eqm);
-    gtm0 = gtm;
-    eqm0 = eqm;
-    cgt += (uint32_t)__builtin_popcount(gtm);
-    ceq += (uint32_t)__builtin_popcount(eqm);
+  if (cached) {
+    // positions with a first digit above the prefix are above thr; only the
+    // run's positions in the prefix bin are compared with thr
+    gtm0 = above_run;
+    uint32_t rest = inbin_run;
+    while (rest) {
+      const int e = __builtin_ctz(rest);
+      rest &= rest - 1u;
+      const uint32_t key = sh.keys[kslot(run0 + e)];
+      gtm0 |= (key > thr ? 1u : 0u) << e;
+      eqm0 |= (key == thr ? 1u : 0u) << e;
+    }
+    cgt = (uint32_t)__builtin_popcount(gtm0);
+    ceq = (uint32_t)__builtin_popcount(eqm0);
+  } else {
+    for (int p0 = run0; p0 < run0 + run_len && p0 < n; p0 += 32) {
+      uint32_t gtm, eqm;
+      masks32(p0, &gtm, &eqm);
+      cgt += (uint32_t)__builtin_popcount(gtm);
+      ceq += (uint32_t)__builtin_popcount(eqm);
+    }
   }
   // winners and ties before this thread's run: for selections below 65536
   // elements one scan of both counts, (> thr) in the high half and (== thr)
