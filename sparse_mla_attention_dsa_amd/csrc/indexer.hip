@@ -143,6 +143,7 @@ constexpr int kStreamBatch = 4;                                  // groups per c
 constexpr int kStreamMaxQLen = 4;                                // rows per request, multi-row units
 constexpr int kStreamMaxChunks = 1024;                           // chunk records per round
 constexpr int kDecodeAhead = 1;                                  // chunks in flight per wave (decode)
+constexpr int64_t kStreamMaxStride = 1LL << 29;                  // logits row bytes stay below 2^31
 
 // Waves per work-group: as many as the registers let one CU hold
 template <int kR, int kAhead> constexpr int stream_waves() { return kR == 1 && kAhead == 1 ? 12 : 8; }
@@ -759,9 +760,12 @@ hipError_t launch_indexer_force(const IndexerParams& p, hipStream_t s) {
 hipError_t launch_indexer_fp8(const IndexerParams& p, hipStream_t s) {
   const int chunks = (p.batch.max_seq_len_k + kIdxChunk - 1) / kIdxChunk;
   if (p.batch.num_rows == 0 || chunks == 0) return hipSuccess;
-  const bool decode = p.batch.cu_seqlens_q == nullptr && p.batch.num_rows <= kStreamMaxUnits;
+  // the stream kernel stores each row through a buffer resource whose range
+  // (stride * 4 bytes) must fit 32 bits
+  const bool stream_stride = p.stride <= kStreamMaxStride;
+  const bool decode = p.batch.cu_seqlens_q == nullptr && p.batch.num_rows <= kStreamMaxUnits && stream_stride;
   const bool multi = p.batch.cu_seqlens_q != nullptr && p.batch.max_seq_len_q <= kStreamMaxQLen &&
-                     2 * p.batch.num_seqs <= kStreamMaxUnits;
+                     2 * p.batch.num_seqs <= kStreamMaxUnits && stream_stride;
   if (decode || multi) {
     // spread over as many CUs as there are chunks for one per wave (a bound
     // from the longest row), and no more work-groups than are resident at

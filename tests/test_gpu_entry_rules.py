@@ -152,3 +152,33 @@ def test_indexer_absent_pages(name, kw):
     assert n_neg > 0, "the broken pages must hold visible positions"
     parity.check_topk_exact(idx, logits, vis, cfg.topk, rows)
     print(f"[rules] indexer {name}: -inf positions {n_neg}, logits err/bound {worst:.3f}", flush=True)
+
+
+def test_indexer_logits_row_stride_beyond_the_stream_kernel():
+    """A logits row stride of more than 2^29 floats (a 2 GiB row) takes the
+    general fp8 kernel instead of the stream kernel, whose per-row store range
+    must fit 32 bits; both give the same scores (same contraction, same
+    summation order)."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_mla_attention_dsa_amd as dsa
+    wl = generate(small_config("wide_stride", seed=231, lens=[3000]), with_mla=False)
+    dev = "cuda"
+    bt = torch.from_numpy(wl.block_table).to(dev)
+    lens = torch.from_numpy(wl.seq_lens_k).to(dev)
+    batch = dsa.make_batch(bt, lens, page_size=wl.cfg.page_size, num_pages=wl.index_cache.shape[0],
+                           max_seq_len_k=int(wl.seq_lens_k.max()))
+    q = torch.from_numpy(wl.q_idx).to(dev).view(torch.float8_e4m3fn)
+    w = torch.from_numpy(wl.w).to(dev)
+    cache = torch.from_numpy(wl.index_cache).to(dev)
+    n = int(wl.seq_lens_k[0])
+    narrow = torch.empty((1, n), dtype=torch.float32, device=dev)
+    dsa.dsa_indexer_logits(batch, q, w, cache, narrow)
+    wide = torch.empty((1, (1 << 29) + 64), dtype=torch.float32, device=dev)
+    print(f"\n[entry] logits row stride {wide.stride(0)} floats", flush=True)
+    dsa.dsa_indexer_logits(batch, q, w, cache, wide)
+    torch.cuda.synchronize()
+    assert torch.equal(wide[0, :n], narrow[0]), "wide-stride scores differ"
+    parity.check_logits(narrow.cpu().numpy(), wl, [0])
+    del wide
+    torch.cuda.empty_cache()
