@@ -308,6 +308,10 @@ def measure(cfg, K, W, graph=True, with_input_side=True, fused=False):
     torch.cuda.synchronize()
     stage_ms = {name: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev]))
                 for j, (name, _) in enumerate(stages)}
+    # per-step spread of the eager pass (each step bracketed by its own events)
+    eager_us = np.array([e[0].elapsed_time(e[-1]) * 1e3 for e in ev])
+    eager = {"p10_us": float(np.percentile(eager_us, 10)), "median_us": float(np.median(eager_us)),
+             "p90_us": float(np.percentile(eager_us, 90)), "steps": int(K)}
     print(f"[bench] {cfg.name}: timed {K} steps: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
 
     input_side = time_input_side(wl, K, stream) if with_input_side else None
@@ -359,6 +363,7 @@ def measure(cfg, K, W, graph=True, with_input_side=True, fused=False):
         "stages": kernels,
         "input_side": input_side,
         "roofline": roofline,
+        "eager_step": eager,
     }
 
 
@@ -420,6 +425,7 @@ def main():
                    "page_size": cfg.page_size, "indexer": f"{cfg.idx_heads}x{cfg.idx_dim} {cfg.idx_kind}",
                    "mla": f"{cfg.mla_heads} heads x {cfg.d_latent}+{cfg.d_rope} {cfg.mla_kind}"},
         "sparse_attn_hbm_gbps": m["stages"]["sparse_mla"]["hbm_gbps"],
+        "eager_step_us": m["eager_step"],
         "stages": m["stages"],
         "input_side": m["input_side"],
         "roofline": m["roofline"],
