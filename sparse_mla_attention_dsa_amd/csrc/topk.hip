@@ -71,6 +71,7 @@ struct TopkShared {
   uint32_t wave_sum[2][kWaves];
   uint32_t sel_bin;
   uint32_t sel_above;
+  uint32_t sel_count;
 };
 
 constexpr int kTkCache = TopkShared<kTkThreads>::kCache;   // 32768 keys
@@ -142,10 +143,11 @@ __device__ __forceinline__ uint32_t block_scan(TopkShared<kThreads>& sh, uint32_
 }
 
 // Largest bin b whose suffix count sum_{b' >= b} hist[b'] reaches `need`; also
-// the count strictly above it.
+// the count strictly above it and the count in it. Ends with a barrier after
+// which the histogram is no longer read.
 template <int kThreads>
 __device__ void select_bin(TopkShared<kThreads>& sh, int nbins, uint32_t need, int buf, uint32_t* bin,
-                           uint32_t* above) {
+                           uint32_t* above, uint32_t* count) {
   const int tid = threadIdx.x;
   const int per = nbins >= kThreads ? nbins / kThreads : 1;
   const int active = nbins / per;
@@ -164,6 +166,7 @@ __device__ void select_bin(TopkShared<kThreads>& sh, int nbins, uint32_t need, i
       if (cum + h >= need) {
         sh.sel_bin = (uint32_t)bb;
         sh.sel_above = cum;
+        sh.sel_count = h;
         break;
       }
       cum += h;
@@ -172,6 +175,7 @@ __device__ void select_bin(TopkShared<kThreads>& sh, int nbins, uint32_t need, i
   __syncthreads();
   *bin = sh.sel_bin;
   *above = sh.sel_above;
+  *count = sh.sel_count;
 }
 
 enum TopkMode { kWholeRow = 0, kChunk = 1, kMerge = 2, kFused = 3 };
@@ -395,15 +399,14 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
     __syncthreads();
   }
   uint32_t need = (uint32_t)k;
-  uint32_t bin, above;
-  select_bin(sh, kTkBins, need, 0, &bin, &above);
+  uint32_t bin, above, count;
+  select_bin(sh, kTkBins, need, 0, &bin, &above, &count);
   uint32_t prefix = bin;
   need -= above;
 
   // ---- level 1 (bits 19..8) among keys whose top 12 bits equal the prefix;
   //      those keys are also collected (unordered) for the last level ----
-  const bool keep = sh.hist[prefix] <= (uint32_t)kCand;   // read before the histogram is cleared
-  __syncthreads();
+  const bool keep = count <= (uint32_t)kCand;
   for (int i = tid; i < kTkBins; i += kThreads) sh.hist[i] = 0;
   if (tid == 0) sh.n_cand = 0;
   __syncthreads();
@@ -477,35 +480,64 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
   }
   if (lane_id() == 0) sh.wave_cand[wave] = wcnt;
   __syncthreads();
-  select_bin(sh, kTkBins, need, 1, &bin, &above);
+  select_bin(sh, kTkBins, need, 1, &bin, &above, &count);
   prefix = (prefix << 12) | bin;
   need -= above;
+  const uint32_t count24 = count;                      // keys sharing the top 24 bits with the k-th
 
   // ---- level 2 (bits 7..0) among keys whose top 24 bits equal the prefix ----
-  for (int i = tid; i < 256; i += kThreads) sh.hist[i] = 0;
-  __syncthreads();
   bool kept = keep;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) kept = kept && sh.wave_cand[w] <= (uint32_t)kTkCandPerWave;
-  if (kept) {
+  uint32_t thr;
+  if (kept && count24 <= (uint32_t)kWave) {
+    // Few keys share the top 24 bits (the usual case): gather them from the
+    // candidate lists into the histogram area (free since the last selection),
+    // then every wave finds the need-th largest by ranking them, one lane per
+    // key, with no further barrier.
+    uint32_t* few = sh.hist;
     const uint32_t nc = sh.wave_cand[wave];            // wave w scans wave w's slots
     for (uint32_t i = lane_id(); i < nc; i += kWave) {
       const uint32_t u = sh.cand[wave * kTkCandPerWave + i];
-      if ((u >> 8) == prefix) atomicAdd(&sh.hist[u & 0xffu], 1u);
+      if ((u >> 8) == prefix) few[atomicAdd(&sh.n_cand, 1u)] = u;
     }
+    __syncthreads();
+    const uint32_t lane = (uint32_t)lane_id();
+    const uint32_t mine = lane < count24 ? few[lane] : 0u;
+    uint32_t gt = 0, ge = 0;                           // keys of the bin above / not below mine
+    for (uint32_t j = 0; j < count24; ++j) {
+      const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)mine, (int)j);
+      gt += kj > mine ? 1u : 0u;
+      ge += kj >= mine ? 1u : 0u;
+    }
+    const uint64_t hit = __ballot(lane < count24 && gt < need && need <= ge);   // lanes holding the k-th key
+    const int src_lane = (int)__builtin_ctzll(hit);
+    thr = (uint32_t)__builtin_amdgcn_readlane((int)mine, src_lane);
+    need -= (uint32_t)__builtin_amdgcn_readlane((int)gt, src_lane);
   } else {
-    for (int i = kTkPer * tid; i < n; i += kTkPer * kThreads) {
-      uint32_t u[kTkPer];
-      load8<kKeys>(src, sh, cached, n, i, u);
+    for (int i = tid; i < 256; i += kThreads) sh.hist[i] = 0;
+    __syncthreads();
+    if (kept) {
+      const uint32_t nc = sh.wave_cand[wave];          // wave w scans wave w's slots
+      for (uint32_t i = lane_id(); i < nc; i += kWave) {
+        const uint32_t u = sh.cand[wave * kTkCandPerWave + i];
+        if ((u >> 8) == prefix) atomicAdd(&sh.hist[u & 0xffu], 1u);
+      }
+    } else {
+      for (int i = kTkPer * tid; i < n; i += kTkPer * kThreads) {
+        uint32_t u[kTkPer];
+        load8<kKeys>(src, sh, cached, n, i, u);
 #pragma unroll
-      for (int e = 0; e < kTkPer; ++e)
-        if (i + e < n && (u[e] >> 8) == prefix) atomicAdd(&sh.hist[u[e] & 0xffu], 1u);
+        for (int e = 0; e < kTkPer; ++e)
+          if (i + e < n && (u[e] >> 8) == prefix) atomicAdd(&sh.hist[u[e] & 0xffu], 1u);
+      }
     }
+    __syncthreads();
+    select_bin(sh, 256, need, 0, &bin, &above, &count);
+    thr = (prefix << 8) | bin;
+    need -= above;
   }
-  __syncthreads();
-  select_bin(sh, 256, need, 0, &bin, &above);
-  const uint32_t thr = (prefix << 8) | bin;
-  need -= above;  // how many keys equal to thr are among the winners (>= 1)
+  // need: how many keys equal to thr are among the winners (>= 1)
 
   // ---- ordered output ----
   // A winner at position p goes to slot #winners before p = (#keys > thr before
