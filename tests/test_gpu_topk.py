@@ -98,3 +98,71 @@ def test_merge_of_more_candidates_than_the_cache():
     candidates, more than the merge's LDS key cache, so the merge selection
     runs uncached."""
     assert _run([340000, 100000, 5000], 3000, _ties, seed=21) > 0
+
+
+# Whole-row selections of rows up to 32,768 long (held in LDS), on value
+# distributions that stress the digit passes: ties on every fourth position,
+# values spread over 80 binary orders of magnitude with infinities, constant
+# rows, and every k regime (short rows, the rank path of the last digit, the
+# last-digit histogram).
+REG_LENGTHS = [1, 2047, 2048, 2049, 4096, 8192, 8193, 9000, 16384, 20000, 24576, 32767, 32768]
+
+
+@pytest.mark.parametrize("values", [_ties, _normal], ids=["ties", "normal"])
+def test_whole_rows_in_lds(values):
+    assert _run(REG_LENGTHS, 2048, values, seed=31) == 0
+
+
+@pytest.mark.parametrize("k", [1, 7, 256, 4096])
+def test_whole_rows_in_lds_k(k):
+    _run([3, 5000, 16385, 20000, 32768], k, _normal, seed=32 + k)
+
+
+def _low_every_fourth(rng, n):
+    """Positions 0 mod 4 far below the rest."""
+    v = rng.standard_normal(n).astype(np.float32)
+    s = np.arange(n) % 4 == 0
+    v[s] = np.float32(-100.0) + rng.standard_normal(int(s.sum())).astype(np.float32)
+    return v
+
+
+def _high_every_fourth(rng, n):
+    """Positions 0 mod 4 equal and far above the rest: the k winners are the
+    first k of their ties."""
+    v = rng.standard_normal(n).astype(np.float32)
+    v[np.arange(n) % 4 == 0] = np.float32(100.0)
+    return v
+
+
+def _shifted_every_fourth(rng, n):
+    """Positions 0 mod 4 a quarter of a standard deviation above the rest."""
+    v = rng.standard_normal(n).astype(np.float32)
+    s = np.arange(n) % 4 == 0
+    v[s] += np.float32(0.25)
+    return v
+
+
+def _wide_exponents(rng, n):
+    """Magnitudes 2^U, U uniform in [-40, 40], random signs, some infinities:
+    the keys spread over many first-digit bins."""
+    v = (np.exp2(rng.uniform(-40, 40, size=n)) * np.where(rng.random(n) < 0.5, -1, 1)).astype(np.float32)
+    v[rng.random(n) < 0.01] = np.float32(np.inf)
+    v[rng.random(n) < 0.01] = np.float32(-np.inf)
+    return v
+
+
+def _constant(rng, n):
+    return np.full(n, np.float32(0.25))
+
+
+@pytest.mark.parametrize("values", [_low_every_fourth, _high_every_fourth, _shifted_every_fourth, _wide_exponents, _constant],
+                         ids=["low-every-fourth", "high-every-fourth", "shifted-every-fourth", "wide-exponents", "constant"])
+def test_whole_rows_skewed_values(values):
+    assert _run([16384, 24576, 32768, 20000, 9000, 8193], 2048, values, seed=41) == 0
+
+
+@pytest.mark.parametrize("values", [_low_every_fourth, _normal], ids=["low-every-fourth", "normal"])
+def test_chunks_and_merge_skewed_values(values):
+    """Few long rows: the 16,384-position chunks and the merge of their
+    candidates on the same value patterns."""
+    assert _run([131072, 70000, 40000], 2048, values, seed=43) > 0
