@@ -71,12 +71,18 @@ __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
 // max / sum of v over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 16-lane
 // groups), with the gfx950 lane swaps (VALU, no LDS round trip); every lane
 // gets the result
+// The maximum is IEEE 754-2019 `maximum` (a NaN input gives NaN), which
+// gfx950 has as v_maximum3_f32; fmaxf would first quiet each input with an
+// extra v_max_f32.
 __device__ __forceinline__ float max_over_groups(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  v = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+
+// IEEE 754-2019 maximum of two floats (NaN propagates; v_maximum3_f32)
+__device__ __forceinline__ float fmaximum(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 __device__ __forceinline__ float sum_over_groups(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);

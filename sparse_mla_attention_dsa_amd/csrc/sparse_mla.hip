@@ -124,6 +124,7 @@ __device__ __forceinline__ void wait_tiles(int tiles, bool five) {
   }
 }
 
+template <bool kPosScale>
 __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
   __shared__ MlaShared sh;
   const BatchView& bv = p.batch;
@@ -212,11 +213,19 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
   // logical chunk col ^ swz(r) of the row. Rows past the split's valid
   // entries re-read its first row (their scores are masked).
   auto fetch_rows = [&](int tile, int (&rid)[kPiecesMax]) {
+    if ((tile + 1) * kMlaTile <= nvalid) {             // uniform: every row of the tile is valid
 #pragma unroll
-    for (int j = 0; j < kPiecesMax; ++j) {
-      const int pc = min(wave + kMlaWaves * j, kPiecesPerTile - 1);
-      const int e = tile * kMlaTile + (64 * pc + lane) / kChunksPerRow;
-      rid[j] = sh.rowid[e < nvalid ? e : 0];
+      for (int j = 0; j < kPiecesMax; ++j) {
+        const int pc = min(wave + kMlaWaves * j, kPiecesPerTile - 1);
+        rid[j] = sh.rowid[tile * kMlaTile + (64 * pc + lane) / kChunksPerRow];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kPiecesMax; ++j) {
+        const int pc = min(wave + kMlaWaves * j, kPiecesPerTile - 1);
+        const int e = tile * kMlaTile + (64 * pc + lane) / kChunksPerRow;
+        rid[j] = sh.rowid[e < nvalid ? e : 0];
+      }
     }
   };
   auto issue_pieces = [&](int tile, const int (&rid)[kPiecesMax], int j0, int j1) {
@@ -323,15 +332,26 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
     // lane's head at contraction indices 8g .. 8g+7 and its rescale factor
     auto softmax = [&](int tile, const f32x4& s0, const f32x4& s1, float* alpha) -> bf16x8 {
       const int rows_left = nvalid - tile * kMlaTile;   // padding rows (last tile only) -> -inf
+      // With a positive scale the scores stay unscaled here: rounding is
+      // monotone, so the maximum of the scaled scores is the scaled maximum,
+      // and the scale enters each exponent through one fma.
       float sv[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sv[i] = (4 * g + i < rows_left) ? s0[i] * scale_log2 : -INFINITY;
-        sv[4 + i] = (16 + 4 * g + i < rows_left) ? s1[i] * scale_log2 : -INFINITY;
+        sv[i] = kPosScale ? s0[i] : s0[i] * scale_log2;
+        sv[4 + i] = kPosScale ? s1[i] : s1[i] * scale_log2;
       }
-      float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                       fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-      mx = max_over_groups(mx);
+      if (rows_left < kMlaTile) {                        // uniform: the last, partial tile
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sv[i] = (4 * g + i < rows_left) ? sv[i] : -INFINITY;
+          sv[4 + i] = (16 + 4 * g + i < rows_left) ? sv[4 + i] : -INFINITY;
+        }
+      }
+      float mx = fmaximum(fmaximum(fmaximum(sv[0], sv[1]), fmaximum(sv[2], sv[3])),
+                          fmaximum(fmaximum(sv[4], sv[5]), fmaximum(sv[6], sv[7])));
+      mx = max_over_groups(mx);                        // a NaN score makes the head's output NaN either way
+      if (kPosScale) mx *= scale_log2;
       *alpha = 1.f;
       if (mx > m_ref + kRescaleThreshold) {
         *alpha = __builtin_amdgcn_exp2f(m_ref - mx);
@@ -341,7 +361,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_bf16_kernel(MlaParams p) {
       float pr[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        pr[i] = __builtin_amdgcn_exp2f(sv[i] - m_ref);
+        pr[i] = __builtin_amdgcn_exp2f(kPosScale ? fmaf(sv[i], scale_log2, -m_ref) : sv[i] - m_ref);
         l_part += pr[i];
       }
       bf16x8 pa;                                         // round to nearest even (v_cvt_pk_bf16_f32)
@@ -645,7 +665,10 @@ hipError_t launch_mla_bf16(const MlaParams& p, hipStream_t s) {
   const int units = T * p.splits;
   const int units_per_xcd = (units + 7) / 8;
   const int64_t blocks = 8LL * units_per_xcd * HG;
-  hipLaunchKernelGGL(mla_bf16_kernel, dim3((unsigned)blocks), dim3(kMlaThreads), 0, s, p);
+  if (p.softmax_scale > 0.f)
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(mla_bf16_kernel<true>), dim3((unsigned)blocks), dim3(kMlaThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(mla_bf16_kernel<false>), dim3((unsigned)blocks), dim3(kMlaThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   return launch_mla_combine_bf16(p, s);

@@ -182,3 +182,35 @@ def test_indexer_logits_row_stride_beyond_the_stream_kernel():
     parity.check_logits(narrow.cpu().numpy(), wl, [0])
     del wide
     torch.cuda.empty_cache()
+
+
+SCALE_CASES = [("bf16", 0.0), ("bf16", -0.06), ("bf16", 0.3), ("fp8", 0.0), ("fp8", -0.06)]
+
+
+@pytest.mark.parametrize("kind,scale", SCALE_CASES, ids=[f"{k}_{s}" for k, s in SCALE_CASES])
+def test_attention_any_softmax_scale(kind, scale):
+    """The attention takes any finite softmax scale: zero (uniform weights over
+    the valid entries), negative (the smallest scores dominate) and positive
+    ones (the kernels take a separate path for positive scales, with the scale
+    folded into the exponent), on decode and prefill rows, against the oracle."""
+    _need_gpu()
+    from dsa_workloads.device import make_step
+    seed = 740 + SCALE_CASES.index((kind, scale))
+    rng = np.random.default_rng(seed)
+    cfg = small_config(f"scale_{kind}_{scale}", seed=seed, topk=2048, lens=[3000, 2600, 700], q_lens=[2, 1, 3],
+                       mla_kind=kind, softmax_scale=scale)
+    wl = generate(cfg, with_indexer=False)
+    vis = parity.visible_of(wl)
+    k = cfg.topk
+    idx = np.full((wl.num_rows, k), -1, dtype=np.int32)
+    for t in range(wl.num_rows):
+        n = min(int(vis[t]), k)
+        idx[t, :n] = np.sort(rng.choice(int(vis[t]), size=n, replace=False))
+    step = make_step(wl)
+    print(f"\n[scale] {kind} softmax_scale={scale}: rows {wl.num_rows}, visible {vis}", flush=True)
+    step.attend(topk_idx=torch.from_numpy(idx).cuda())
+    torch.cuda.synchronize()
+    out = step.out.float().cpu().numpy()
+    lse = step.lse.cpu().numpy()
+    worst = parity.check_attention(out, lse, wl, idx, list(range(wl.num_rows)))
+    print(f"[scale] {kind} softmax_scale={scale}: attention err/bound {worst:.3f}", flush=True)
