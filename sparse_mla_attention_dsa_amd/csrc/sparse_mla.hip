@@ -45,6 +45,8 @@
 // the head groups of one (row, split) unit, and neighbouring units, land on
 // the same XCD (work-group i runs on XCD i % 8) and share the gathered rows
 // through that XCD's L2.
+#include <cfloat>
+
 #include "device_common.h"
 #include "dsa_internal.h"
 
@@ -665,7 +667,9 @@ hipError_t launch_mla_bf16(const MlaParams& p, hipStream_t s) {
   const int units = T * p.splits;
   const int units_per_xcd = (units + 7) / 8;
   const int64_t blocks = 8LL * units_per_xcd * HG;
-  if (p.softmax_scale > 0.f)
+  // the positive-scale path needs a normal scale: a padding row's -inf times
+  // a zero (flushed) scale would give NaN in its exponent
+  if (p.softmax_scale * kLog2e >= FLT_MIN)
     hipLaunchKernelGGL(HIP_KERNEL_NAME(mla_bf16_kernel<true>), dim3((unsigned)blocks), dim3(kMlaThreads), 0, s, p);
   else
     hipLaunchKernelGGL(HIP_KERNEL_NAME(mla_bf16_kernel<false>), dim3((unsigned)blocks), dim3(kMlaThreads), 0, s, p);

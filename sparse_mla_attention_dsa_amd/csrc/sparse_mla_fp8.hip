@@ -30,6 +30,8 @@
 // search over chunk swizzles and row orders: no swizzle serves both read
 // patterns with the plain row order). P rows are padded to 72 elements so that
 // the P^T reads of sixteen heads fall on distinct banks.
+#include <cfloat>
+
 #include "device_common.h"
 #include "dsa_internal.h"
 
@@ -114,6 +116,7 @@ __device__ __forceinline__ void wait_tiles8(int tiles, bool five) {
   }
 }
 
+template <bool kPosScale>
 __global__ __launch_bounds__(kF8Threads) void mla_fp8_kernel(MlaParams p) {
   __shared__ F8Shared sh;
   const BatchView& bv = p.batch;
@@ -201,11 +204,19 @@ __global__ __launch_bounds__(kF8Threads) void mla_fp8_kernel(MlaParams p) {
   // position col, holding the row's logical chunk col ^ swz8(r). Rows past
   // the split's valid entries re-read its first row (their scores are masked).
   auto fetch_rows = [&](int tile, int (&rid)[kF8PiecesMax]) {
+    if ((tile + 1) * kF8Tile <= nvalid) {              // uniform: every row of the tile is valid
 #pragma unroll
-    for (int j = 0; j < kF8PiecesMax; ++j) {
-      const int pc = min(wave + kF8Waves * j, kF8Pieces - 1);
-      const int e = tile * kF8Tile + (64 * pc + lane) / kF8Chunks;
-      rid[j] = sh.rowid[e < nvalid ? e : 0];
+      for (int j = 0; j < kF8PiecesMax; ++j) {
+        const int pc = min(wave + kF8Waves * j, kF8Pieces - 1);
+        rid[j] = sh.rowid[tile * kF8Tile + (64 * pc + lane) / kF8Chunks];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kF8PiecesMax; ++j) {
+        const int pc = min(wave + kF8Waves * j, kF8Pieces - 1);
+        const int e = tile * kF8Tile + (64 * pc + lane) / kF8Chunks;
+        rid[j] = sh.rowid[e < nvalid ? e : 0];
+      }
     }
   };
   auto issue_pieces = [&](int tile, const int (&rid)[kF8PiecesMax], int j0, int j1) {
@@ -301,19 +312,29 @@ __global__ __launch_bounds__(kF8Threads) void mla_fp8_kernel(MlaParams p) {
     // (pa[rb][0]: tile rows 16 rb + 2 g, + 1; pa[rb][1]: 16 rb + 8 + 2 g, + 1)
     // and its head's rescale factor
     auto softmax = [&](int tile, const f32x4 (&sacc)[kF8RowBlocks], bf16x2 (&pa)[kF8RowBlocks][2], float* alpha) {
+      // With a positive scale the scores stay unscaled here: rounding is
+      // monotone, so the maximum of the scaled scores is the scaled maximum,
+      // and the scale enters each exponent through one fma.
       const int rows_left = nvalid - tile * kF8Tile;
       float sv[4 * kF8RowBlocks];
-      float mx = -INFINITY;
 #pragma unroll
       for (int rb = 0; rb < kF8RowBlocks; ++rb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 16 * rb + 2 * g + (i >> 1) + 8 * (i & 1);
-          const float v = (row < rows_left) ? sacc[rb][i] * scale_log2 : -INFINITY;
-          sv[4 * rb + i] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = max_over_groups(mx);
+        for (int i = 0; i < 4; ++i) sv[4 * rb + i] = kPosScale ? sacc[rb][i] : sacc[rb][i] * scale_log2;
+      if (rows_left < kF8Tile) {                         // uniform: the last, partial tile
+#pragma unroll
+        for (int rb = 0; rb < kF8RowBlocks; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = 16 * rb + 2 * g + (i >> 1) + 8 * (i & 1);
+            sv[4 * rb + i] = (row < rows_left) ? sv[4 * rb + i] : -INFINITY;
+          }
+      }
+      float mx = sv[0];
+#pragma unroll
+      for (int i = 1; i < 4 * kF8RowBlocks; ++i) mx = fmaximum(mx, sv[i]);
+      mx = max_over_groups(mx);                        // a NaN score makes the head's output NaN either way
+      if (kPosScale) mx *= scale_log2;
       *alpha = 1.f;
       if (mx > m_ref + kF8RescaleThreshold) {
         *alpha = __builtin_amdgcn_exp2f(m_ref - mx);
@@ -325,7 +346,7 @@ __global__ __launch_bounds__(kF8Threads) void mla_fp8_kernel(MlaParams p) {
         float pr[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pr[i] = __builtin_amdgcn_exp2f(sv[4 * rb + i] - m_ref);
+          pr[i] = __builtin_amdgcn_exp2f(kPosScale ? fmaf(sv[4 * rb + i], scale_log2, -m_ref) : sv[4 * rb + i] - m_ref);
           l_part += pr[i];
         }
         pa[rb][0] = __builtin_convertvector(f32x2{pr[0], pr[2]}, bf16x2);   // rows 2 g, 2 g + 1
@@ -487,7 +508,13 @@ hipError_t launch_mla_fp8(const MlaParams& p, hipStream_t s) {
   const int units = T * p.splits;
   const int units_per_xcd = (units + 7) / 8;
   const int64_t blocks = 8LL * units_per_xcd * HG;
-  hipLaunchKernelGGL(mla_fp8_kernel, dim3((unsigned)blocks), dim3(kF8Threads), 0, s, p);
+  // the positive-scale path needs a normal scale (the kernel's product, in
+  // the same order): a padding row's -inf times a zero (flushed) scale would
+  // give NaN in its exponent
+  if (p.softmax_scale * p.q_scale * p.kv_scale * kF8Log2e >= FLT_MIN)
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(mla_fp8_kernel<true>), dim3((unsigned)blocks), dim3(kF8Threads), 0, s, p);
+  else
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(mla_fp8_kernel<false>), dim3((unsigned)blocks), dim3(kF8Threads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   return launch_mla_combine_bf16(p, s);

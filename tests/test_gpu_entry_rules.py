@@ -184,15 +184,16 @@ def test_indexer_logits_row_stride_beyond_the_stream_kernel():
     torch.cuda.empty_cache()
 
 
-SCALE_CASES = [("bf16", 0.0), ("bf16", -0.06), ("bf16", 0.3), ("fp8", 0.0), ("fp8", -0.06)]
+SCALE_CASES = [("bf16", 0.0), ("bf16", -0.06), ("bf16", 0.3), ("bf16", 1e-39), ("fp8", 0.0), ("fp8", -0.06), ("fp8", 0.3), ("fp8", 1e-39)]
 
 
 @pytest.mark.parametrize("kind,scale", SCALE_CASES, ids=[f"{k}_{s}" for k, s in SCALE_CASES])
 def test_attention_any_softmax_scale(kind, scale):
     """The attention takes any finite softmax scale: zero (uniform weights over
-    the valid entries), negative (the smallest scores dominate) and positive
-    ones (the kernels take a separate path for positive scales, with the scale
-    folded into the exponent), on decode and prefill rows, against the oracle."""
+    the valid entries), negative (the smallest scores dominate), positive ones
+    (the kernels take a separate path for positive normal scales, with the
+    scale folded into the exponent) and a subnormal one (the general path), on
+    decode and prefill rows whose last tiles are partial, against the oracle."""
     _need_gpu()
     from dsa_workloads.device import make_step
     seed = 740 + SCALE_CASES.index((kind, scale))
