@@ -92,12 +92,15 @@ def test_full_single_decode_8k():
 
 
 def test_full_ragged_batch64_sampled():
-    """Logits and attention on sampled rows; top-k bit-exact on the GPU's own
-    logits for all 64 rows (the oracle's selection is cheap)."""
+    """Logits and attention on sampled rows (the shortest and longest requests
+    and the quartiles of the lengths); top-k bit-exact on the GPU's own logits
+    for all 64 rows (the oracle's selection is cheap)."""
     cfg = CONFIGS["decode_b64_ragged"]
     wl = generate(cfg, with_mla=False)
     lens = wl.seq_lens_k
-    rows = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 17})
+    order = np.argsort(lens, kind="stable")
+    rows = sorted({int(order[0]), int(order[len(order) // 4]), int(order[len(order) // 2]),
+                   int(order[3 * len(order) // 4]), int(order[-1]), 17})
     wl, _, h = _full_check(cfg, rows=rows)
     parity.check_topk_exact(h["topk"], h["logits"], parity.visible_of(wl), cfg.topk, range(wl.num_rows))
 
@@ -122,7 +125,11 @@ def test_full_multi_token_decode_x4_sampled():
 
 
 def test_full_long_context_128k_sampled():
-    _full_check(CONFIGS["decode_b8_128k"], rows=[0, 5])
+    """Logits and attention on two of the eight 131,072-key rows; top-k (the
+    two-phase selection) bit-exact on the GPU's own logits for all eight."""
+    cfg = CONFIGS["decode_b8_128k"]
+    wl, _, h = _full_check(cfg, rows=[0, 5])
+    parity.check_topk_exact(h["topk"], h["logits"], parity.visible_of(wl), cfg.topk, range(wl.num_rows))
 
 
 def test_full_multi_token_decode_sampled():
@@ -131,7 +138,8 @@ def test_full_multi_token_decode_sampled():
     lens = wl.seq_lens_k
     b_min, b_max = int(np.argmin(lens)), int(np.argmax(lens))
     rows = sorted({2 * b_min, 2 * b_min + 1, 2 * b_max, 2 * b_max + 1, 35})
-    _full_check(cfg, rows=rows)
+    wl, _, h = _full_check(cfg, rows=rows)
+    parity.check_topk_exact(h["topk"], h["logits"], parity.visible_of(wl), cfg.topk, range(wl.num_rows))
 
 
 def test_full_ragged_batch64_fp8_cache_sampled():
@@ -139,7 +147,8 @@ def test_full_ragged_batch64_fp8_cache_sampled():
     wl = generate(cfg, with_mla=False)
     lens = wl.seq_lens_k
     rows = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 40})
-    _full_check(cfg, rows=rows)
+    wl, _, h = _full_check(cfg, rows=rows)
+    parity.check_topk_exact(h["topk"], h["logits"], parity.visible_of(wl), cfg.topk, range(wl.num_rows))
 
 
 def test_decode_batch32_four_splits_sampled():
@@ -151,7 +160,11 @@ def test_decode_batch32_four_splits_sampled():
 
 
 def test_full_prefill_sampled():
-    _full_check(CONFIGS["prefill_4k_on_16k"], rows=[0, 1, 2047, 4094, 4095])
+    """Logits and attention on sampled rows; top-k bit-exact on the GPU's own
+    logits for all 4,096 rows (about 2 ms of CPU per row)."""
+    cfg = CONFIGS["prefill_4k_on_16k"]
+    wl, _, h = _full_check(cfg, rows=[0, 1, 2047, 4094, 4095])
+    parity.check_topk_exact(h["topk"], h["logits"], parity.visible_of(wl), cfg.topk, range(wl.num_rows))
 
 
 def _shared_pool_indexer(seed, lens, q_lens=None, pool=320, check_rows=(), absent=False):
