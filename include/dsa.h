@@ -260,6 +260,8 @@ dsa_status_t dsa_indexer_topk(const dsa_batch_t *batch,
  *           d_latent + d_rope <= 1024, d_latent <= 512. (An fp8 cache goes
  *           through sparse_mla_*_fp8; FP8_E4M3 here is UNSUPPORTED.)
  * topk_idx: [T, k] int32, 1 <= k <= 4096.
+ * softmax_scale: any finite value whose product with log2(e) is finite
+ *           (DSA_ERR_INVALID_ARGUMENT otherwise); zero gives uniform weights.
  * out:      [T, Hm, d_latent] in dtype.   lse: [T, Hm] fp32, may be NULL.
  * workspace: at least dsa_workspace_bytes(DSA_OP_MLA_DECODE or _PREFILL, ...)
  *           bytes of device memory (split-KV partial results); NULL if that is 0.
@@ -302,7 +304,8 @@ dsa_status_t sparse_mla_prefill(const dsa_batch_t *batch,
  * selection -> out 0 and lse -inf).
  * q:        [T, Hm, 576] codes (512 latent, then 64 rope), 16-byte aligned rows.
  * kv_cache: [num_pages, P, 576] codes (576 bytes per cached row).
- * Hm a multiple of 64, d_latent 512, d_rope 64; q_scale, kv_scale finite, > 0.
+ * Hm a multiple of 64, d_latent 512, d_rope 64; q_scale, kv_scale finite, > 0;
+ * softmax_scale * q_scale * kv_scale * log2(e) finite.
  * out:      [T, Hm, 512] bf16.   lse: [T, Hm] fp32, may be NULL.
  * workspace: at least dsa_workspace_bytes(DSA_OP_MLA_DECODE or _PREFILL, ...,
  *           DSA_FP8_E4M3) bytes (split partials; always at least two splits

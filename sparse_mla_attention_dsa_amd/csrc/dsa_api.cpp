@@ -148,6 +148,15 @@ dsa_status_t run_mla(const dsa_batch_t* batch, bool decode, const void* q, const
     return fail(DSA_ERR_INVALID_ARGUMENT, "softmax_scale is not finite");
   if (!(q_scale > 0.f && q_scale < INFINITY && kv_scale > 0.f && kv_scale < INFINITY))
     return fail(DSA_ERR_INVALID_ARGUMENT, "q_scale / kv_scale must be finite and positive");
+  {
+    // the kernels work in base 2 with the scale times log2(e) (times the fp8
+    // scales), multiplied in this order in fp32: it must stay finite
+    const volatile float log2e = 1.4426950408889634f;
+    const float s2 = plan.fp8 ? softmax_scale * q_scale * kv_scale * log2e : softmax_scale * log2e;
+    if (!(s2 > -INFINITY && s2 < INFINITY))
+      return fail(DSA_ERR_INVALID_ARGUMENT, "softmax_scale overflows in base 2 (times log2(e)%s)",
+                  plan.fp8 ? " and the fp8 scales" : "");
+  }
   if (bv.num_rows > 0 && (!q || !kv_cache || !topk_idx || !out))
     return fail(DSA_ERR_INVALID_ARGUMENT, "q / kv_cache / topk_idx / out is NULL");
   if (workspace_bytes < plan.workspace)

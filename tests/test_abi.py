@@ -161,6 +161,9 @@ def test_mla_validation(L):
     assert _mla(L, dec, dtype=dsa.DSA_FP8_E4M3) == dsa.DSA_ERR_UNSUPPORTED
     assert _mla(L, dec, k=0) == dsa.DSA_ERR_INVALID_ARGUMENT
     assert _mla(L, dec, scale=float("nan")) == dsa.DSA_ERR_INVALID_ARGUMENT
+    # finite, but the kernels' base-2 scale (times log2(e)) would overflow
+    assert _mla(L, dec, scale=3e38) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert _mla(L, dec, scale=-3e38) == dsa.DSA_ERR_INVALID_ARGUMENT
     assert _mla(L, dec, nullout=True, ws=ctypes.c_void_p(0x50), wsb=need) == dsa.DSA_ERR_INVALID_ARGUMENT
     # decode needs cu_seqlens_q == NULL, prefill needs it
     pre = _batch(num_seqs=1, num_rows=4096, max_seq_len_q=4096, cu_seqlens_q=0x6000)
@@ -245,14 +248,17 @@ def test_fp8_attention_entry_points_validate_on_the_host(L):
     b = _batch()
     V = ctypes.c_void_p
 
-    def call(q_scale=0.02, kv_scale=0.01, H=128, Dl=512, Dr=64, ws=None, wsb=0):
+    def call(q_scale=0.02, kv_scale=0.01, H=128, Dl=512, Dr=64, ws=None, wsb=0, scale=0.07):
         return L.sparse_mla_decode_fp8(ctypes.byref(b), V(0x10), q_scale, V(0x20), kv_scale, V(0x30), 2048,
-                                       H, Dl, Dr, 0.07, V(0x40), None, ws, wsb, None)
+                                       H, Dl, Dr, scale, V(0x40), None, ws, wsb, None)
     need = L.dsa_workspace_bytes(dsa.DSA_OP_MLA_DECODE, ctypes.byref(b), 2048, 128, 512, dsa.DSA_FP8_E4M3)
     rows = b.num_rows
     assert need >= rows * 2 * 128 * (512 * 2 + 4)                      # at least two splits
     assert call(q_scale=0.0, ws=V(0x1000), wsb=need) == dsa.DSA_ERR_INVALID_ARGUMENT
     assert call(kv_scale=float("inf"), ws=V(0x1000), wsb=need) == dsa.DSA_ERR_INVALID_ARGUMENT
+    # each scale finite, their product with log2(e) not
+    assert call(q_scale=1e20, kv_scale=1e20, ws=V(0x1000), wsb=need) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert call(scale=3e38, q_scale=1.0, kv_scale=1.0, ws=V(0x1000), wsb=need) == dsa.DSA_ERR_INVALID_ARGUMENT
     assert call(H=96, ws=V(0x1000), wsb=need) == dsa.DSA_ERR_UNSUPPORTED
     assert call(Dr=32, ws=V(0x1000), wsb=need) == dsa.DSA_ERR_UNSUPPORTED
     assert call(ws=V(0x1000), wsb=need - 1) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
